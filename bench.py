@@ -1,0 +1,189 @@
+"""Benchmark: padding-free MoE layer forward + backward on one MI355X.
+
+Workload (default): the DeepSeek-MoE-16B-like layer -- 4096 tokens, d = 2048,
+64 routed SwiGLU experts of hidden 1408, top-6, plus 2 always-on shared experts
+of hidden 1408, bf16 with fp32 accumulation, Gaussian synthetic inputs.  One
+step is the whole hot path: route, PFT build, dispatch, routed and shared
+expert FFN, combine, and the backward of each (combine, experts, dispatch,
+router).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: useful TFLOPS (router + routed + shared expert GEMMs on
+unpadded rows; backward GEMMs count twice the forward), tokens/s, the roofline
+of the dominant kernel (the expert up-projection), and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd useful TFLOPS + tokens/s on 1 MI355X (DeepSeek-MoE shape)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsmoe16b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0: pick for ~10-30 s)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
+              f"across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads
+    import padding_free_expert_amd as xm
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+    assert xm.xmoe_query_device(0), "cuda:0 is not gfx950"
+    wl = workloads.get(args.workload)
+    assert wl.dtype == "bf16"
+    inp = workloads.generate(wl, device="cuda", backward=True)
+    weights = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias")
+               if k in inp}
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True)
+    x, dy = inp["x"], inp["dy"]
+    stream = torch.cuda.current_stream()
+
+    def step(hook=None):
+        layer.forward(x, hook=hook)
+        layer.backward(dy, hook=hook)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = max(gpu_ms, wall * 1e3 / args.steps)
+    flops = wl.useful_flops()
+    tflops = flops["total"] / (ms * 1e-3) / 1e12
+    tok_s = wl.T / (ms * 1e-3)
+
+    # per-call breakdown: events between library calls, averaged over a few steps
+    names, evs = [], []
+
+    def hook(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        names.append(name)
+        evs.append(e)
+
+    reps = 5
+    breakdown = {}
+    for _ in range(reps):
+        names.clear()
+        evs.clear()
+        start = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        step(hook)
+        torch.cuda.synchronize()
+        prev = start
+        for n, e in zip(names, evs):
+            breakdown[n] = breakdown.get(n, 0.0) + prev.elapsed_time(e) / reps
+            prev = e
+
+    # roofline of the dominant kernel: the up-projection (W1|W3 + SwiGLU), launched
+    # once for the routed experts and once for the shared experts per step
+    R, d, h = wl.R, wl.d, wl.h
+    up_launches = [(layer.xs, weights["w1"], weights["w3"], layer.pft.expert_offsets, layer.act, layer.h13,
+                    4.0 * R * d * h)]
+    if layer.shared:
+        hs = layer.hs
+        up_launches.append((x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0), layer.sh_off,
+                            layer.sh_act, layer.sh_h13, 4.0 * wl.T * d * hs))
+    n_rep = 20
+    tot_ms, tot_flop, per = 0.0, 0.0, []
+    for (a, w1, w3, off, act, h13, fl) in up_launches:
+        for _ in range(3):
+            xm.xmoe_expert_ffn_up(a, w1, w3, off, act, h13)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_rep):
+            xm.xmoe_expert_ffn_up(a, w1, w3, off, act, h13)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / n_rep
+        per.append({"flop": fl, "avg_ms": t, "tflops": fl / (t * 1e-3) / 1e12})
+        tot_ms += t
+        tot_flop += fl
+    achieved = tot_flop / (tot_ms * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_mfma_kernel<128,128,64,2,2,2,...,EPI_SWIGLU> (expert up-projection)",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches)}
+
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "h": wl.h, "k": wl.k,
+                      "n_shared": wl.n_shared, "h_shared": wl.h_shared, "passes": "fwd+bwd"},
+           "tokens_per_s": round(tok_s, 1), "gpu_ms_per_step": round(gpu_ms, 4),
+           "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+           "useful_gflop_per_step": round(flops["total"] / 1e9, 2),
+           "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
+           "roofline": roofline}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, sample_tokens):
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
+    same inputs: full forward and backward (routing, experts, shared experts,
+    combine, all gradients) for those tokens; throughput scaled per token."""
+    import numpy as np
+    import torch
+
+    import oracle as orc
+
+    cores = len(os.sched_getaffinity(0))
+    orc.set_threads(cores)
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    n = sample_tokens or 256
+    o = {k: bits(v) for k, v in inp.items() if v is not None and k not in ("logit_bias", "select_bias")}
+    for k in ("logit_bias", "select_bias"):
+        if inp.get(k) is not None:
+            o[k] = inp[k].cpu().numpy()
+    o["x"] = o["x"][:n]
+    o["dy"] = o["dy"][:n]
+    t0 = time.perf_counter()
+    fwd = orc.layer_forward(o, wl.k, 1, wl.inv_tau, n_shared=wl.n_shared)
+    orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared)
+    dt = time.perf_counter() - t0
+    sub = wl.__class__(**{**wl.__dict__, "T": n})
+    fl = sub.useful_flops()["total"]
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS", "cores": orc.get_threads(), "kind": "oracle",
+            "sample": f"{n} of {wl.T} tokens, full forward+backward incl. all weight gradients",
+            "seconds": round(dt, 2), "tokens_per_s": round(n / dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

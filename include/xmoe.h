@@ -1,0 +1,267 @@
+/*
+ * xmoe.h -- C ABI of libxmoe.so, the padding-free MoE layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer follows the X-MoE pages:
+ *   - "5.4 MoE模型在分布式训练中的应用", section 训练流程: gate scores per token,
+ *     dispatch tokens to experts, each expert processes its tokens, combine the
+ *     results back to the owning token; the backward runs the reverse path.
+ *   - X-MoE article (adg.csdn.net), section 2.1.1 "PFT数据结构创新": the
+ *     Padding-Free Token buffer (PFT) replaces fixed-capacity expert buffers:
+ *     token_ids, expert_ids, tokens_per_expert, combine_weights and the token
+ *     rows themselves; no padding and no dropped tokens.
+ *   - same article, section 2.1.2 "跨平台核函数优化": a gather that copies row
+ *     token_ids[r] of the input into row r, and expert GEMMs over each expert's
+ *     own rows only (no alignment to a maximum capacity).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is caller-owned DEVICE memory (except the xmoe_pft
+ *     struct itself, a host struct of device pointers read during the call).
+ *     The library never allocates, frees or synchronises; it keeps no state
+ *     beyond its loaded kernels and a per-device architecture check.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Each call
+ *     validates its arguments on the host, enqueues its kernels on `stream`
+ *     and returns without waiting.
+ *   - Matrices are row-major and densely packed.  Sizes are int64_t or int32_t
+ *     as declared; all address arithmetic is 64-bit.
+ *   - Errors: a call that fails validation returns before launching anything
+ *     and has no side effect: XMOE_ERR_INVALID_VALUE (NULL required pointer,
+ *     size out of range, k > E, ...), XMOE_ERR_UNSUPPORTED (dtype, a size that
+ *     is not a multiple of 8 where 16-byte vectors need it, a pointer not
+ *     16-byte aligned, a device that is not gfx950), XMOE_ERR_WORKSPACE
+ *     (workspace too small).  A launch failure returns XMOE_ERR_HIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation, as for any
+ *     HIP work.  xmoe_last_error() returns the calling thread's last message.
+ *   - Outputs must not alias inputs unless stated.  Calls are thread-safe;
+ *     calls on different streams may overlap when their buffers do not alias.
+ *   - dtype XMOE_BF16: bf16 inputs and outputs, fp32 accumulation, one
+ *     round-to-nearest-even per stored value.  XMOE_F32: fp32 throughout.
+ *     Router scores, probabilities and weights are always fp32.
+ *   - Results are deterministic: no floating-point atomics; every sum runs in
+ *     a fixed order, so identical inputs give bitwise identical outputs.
+ *
+ * Notation: T tokens, d model width, E routed experts, h expert hidden width,
+ * k experts per token, R = T*k PFT rows.
+ */
+#ifndef XMOE_H_
+#define XMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    XMOE_OK = 0,
+    XMOE_ERR_INVALID_VALUE = 1,
+    XMOE_ERR_UNSUPPORTED = 2,
+    XMOE_ERR_WORKSPACE = 3,
+    XMOE_ERR_HIP = 4
+} xmoe_status;
+
+typedef enum { XMOE_F32 = 0, XMOE_BF16 = 1 } xmoe_dtype;
+
+/*
+ * The Padding-Free Token buffer (X-MoE article, section 2.1.1), one row per
+ * (token, chosen expert) pair, rows ordered by (expert ascending, token
+ * ascending) -- the order the article's per-expert GEMM visits them
+ * (section 2.1.2).  All pointers are device arrays owned by the caller.
+ *   token_ids[r]          input position of row r                     [R]
+ *   expert_ids[r]         expert of row r                             [R]
+ *   tokens_per_expert[e]  rows of expert e (0 allowed)                [E]
+ *   expert_offsets[e]     first row of expert e; [E] == R             [E+1]
+ *   combine_weights[r]    router weight of row r (fp32)               [R]
+ *   slot_to_row[t*k+j]    row holding token t's j-th choice           [R]
+ * slot_to_row is the inverse of (token_ids, slot); it lets the combine and the
+ * dispatch work token by token without atomics.  The PFT's token rows ("x" on
+ * the page) are the separate `xs` buffer of xmoe_dispatch.
+ */
+typedef struct {
+    int32_t *token_ids;
+    int32_t *expert_ids;
+    int32_t *tokens_per_expert;
+    int32_t *expert_offsets;
+    float *combine_weights;
+    int32_t *slot_to_row;
+} xmoe_pft;
+
+/* Last error message of the calling thread ("" after success). */
+const char *xmoe_last_error(void);
+
+/* Library ABI version (major*100 + minor). */
+int xmoe_version(void);
+
+/*
+ * Query device `ordinal`: *is_gfx950 = 1 when its architecture is gfx950.
+ * Returns XMOE_ERR_HIP if the device cannot be queried.
+ */
+xmoe_status xmoe_query_device(int ordinal, int *is_gfx950);
+
+/* ------------------------------------------------------------------ forward */
+
+/*
+ * Gate ("5.4 MoE模型在分布式训练中的应用", section 训练流程, step a: gate scores
+ * per token; X-MoE notes "略读笔记90", section 需求: large top-k routing).
+ *   z = x[t] . wg                    (x [T,d], wg [d,E], fp32 accumulation)
+ *   s = z * inv_temperature + logit_bias[e]             -> logits [T,E] (fp32)
+ *   p = softmax over the E experts of s
+ *   sel = s + select_bias[e]         (selection only; never in the weights)
+ *   topk_ids[t, j] = the j-th largest sel, ties to the lower expert index
+ *   topk_w[t, j]   = p[t, topk_ids[t, j]]   (not renormalised)
+ * logit_bias / select_bias: fp32 [E] or NULL.  logits (fp32 [T,E]) is required:
+ * it is the softmax input the backward needs.  With XMOE_F32 each logit is one
+ * fused multiply-add per feature in ascending order; with XMOE_BF16 the sum
+ * runs on bf16 matrix cores with fp32 accumulation.
+ * Limits: 1 <= k <= E <= 1024, d >= 1; bf16 needs d % 8 == 0 and E % 8 == 0.
+ */
+xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t T, int32_t d,
+                       int32_t E, int32_t k, float inv_temperature, const float *logit_bias,
+                       const float *select_bias, int32_t *topk_ids, float *topk_w, float *logits,
+                       void *stream);
+
+/* Workspace bytes xmoe_build_pft needs for these sizes (0 if invalid). */
+size_t xmoe_build_pft_workspace_size(int64_t T, int32_t E, int32_t k);
+
+/*
+ * Build the PFT (X-MoE article, section 2.1.1) from a routing result: a
+ * per-block expert histogram, an exclusive scan, then a stable scatter that
+ * gives row r = offsets[e] + (number of earlier tokens that chose e).  Fills
+ * every field of *pft; combine_weights are bit-for-bit copies of topk_w.
+ * Every token appears exactly k times; nothing is padded or dropped.
+ * topk_ids must be valid (each in [0,E), distinct within a token); for invalid
+ * ids the buffer contents are unspecified but every write stays in bounds.
+ * workspace: device, >= xmoe_build_pft_workspace_size(T,E,k) bytes, 16-byte
+ * aligned; its contents need no initialisation and are dead after the call.
+ * Limits: 1 <= k <= E <= 1024, T*k < 2^31.
+ */
+xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E,
+                           int32_t k, const xmoe_pft *pft, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * Dispatch = the PFT gather (X-MoE article, section 2.1.2):
+ *   xs[r, :] = x[token_ids[r], :]   for every PFT row r     (xs [R,d])
+ * Carried out token by token through slot_to_row (each input row is read once
+ * and written to its k rows), which writes exactly the same rows.  Exact copy.
+ * Needs pft->slot_to_row.  d % 8 == 0 (bf16) or d % 4 == 0 (fp32).
+ */
+xmoe_status xmoe_dispatch(const void *x, xmoe_dtype dtype, int64_t T, int32_t d, int32_t k,
+                          const xmoe_pft *pft, void *xs, void *stream);
+
+/*
+ * Up-projection of the SwiGLU experts over the expert-sorted rows (X-MoE
+ * article, section 2.1.2: each expert multiplies only its own rows, no
+ * padding).  For each expert e and each row r in [offsets[e], offsets[e+1]):
+ *   H1 = xs[r] . w1[e],  H3 = xs[r] . w3[e]   (w1, w3 [E,d,h])
+ *   act[r] = silu(H1) * H3,  silu(a) = a / (1 + exp(-a))           (act [rows,h])
+ *   h13[r] = [H1 | H3] rounded to the dtype, if h13 != NULL       (h13 [rows,2h])
+ * expert_offsets: DEVICE int32 [E+1], non-decreasing, offsets[0] == 0,
+ * offsets[E] == rows (segments are clamped to [0, rows]).  The launch is sized
+ * on the host from `rows` and E alone; the tile scheduler reads the offsets on
+ * the device, so nothing is copied back.  Empty experts cost nothing.
+ * Limits: d, h multiples of 8; E <= 1024; rows < 2^31.
+ */
+xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, xmoe_dtype dtype,
+                               const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d,
+                               int32_t h, void *act, void *h13, void *stream);
+
+/*
+ * Down-projection: ye[r] = act[r] . w2[e] for the rows of expert e
+ * (w2 [E,h,d], act [rows,h], ye [rows,d]).  Same offsets and limits as
+ * xmoe_expert_ffn_up.
+ */
+xmoe_status xmoe_expert_ffn_down(const void *act, const void *w2, xmoe_dtype dtype,
+                                 const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d,
+                                 int32_t h, void *ye, void *stream);
+
+/*
+ * Whole expert FFN: xmoe_expert_ffn_up followed by xmoe_expert_ffn_down.
+ * act [rows,h] is required (it is the down-projection's input and the
+ * backward's); h13 may be NULL for a forward-only pass.
+ * Shared (always-on) experts run through the same call with E = 1,
+ * offsets = {0, T}, xs = x; several shared experts of width h_s are one call
+ * of width n*h_s with their weights side by side along the hidden axis.
+ */
+xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, const void *w2,
+                            xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                            int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *ye,
+                            void *stream);
+
+/*
+ * Combine ("5.4 MoE模型在分布式训练中的应用", section 专家并行: results return to
+ * the owning token; X-MoE article, section 2.1.1: combine_weights):
+ *   y[t] = sum_{j=0..k-1} combine_weights[r_j] * ye[r_j]  (+ y_add[t]),
+ *   r_j = slot_to_row[t*k + j]
+ * summed in fp32 in slot order and rounded once.  y_add [T,d] may be NULL
+ * (the shared experts' output goes here).  No atomics.
+ */
+xmoe_status xmoe_combine(const void *ye, const xmoe_pft *pft, int64_t T, int32_t d, int32_t k,
+                         xmoe_dtype dtype, const void *y_add, void *y, void *stream);
+
+/* ----------------------------------------------------------------- backward */
+
+/*
+ * Backward of the combine for the upstream gradient dy [T,d]:
+ *   dye[r]        = combine_weights[r] * dy[token_ids[r]]          (dye [R,d])
+ *   dtopk_w[t, j] = < dy[t], ye[slot_to_row[t*k+j]] >              (fp32 [T,k])
+ * Token by token: dy[t] is read once.
+ */
+xmoe_status xmoe_combine_bwd(const void *dy, const void *ye, const xmoe_pft *pft, int64_t T,
+                             int32_t d, int32_t k, xmoe_dtype dtype, void *dye, float *dtopk_w,
+                             void *stream);
+
+/*
+ * Backward of the SwiGLU experts, per expert, given dye [rows,d]:
+ *   dA  = dye . w2[e]^T
+ *   dH1 = dA * H3 * sig(H1) * (1 + H1 * (1 - sig(H1))),  dH3 = dA * silu(H1)
+ *         -> dh13 = [dH1 | dH3]                                   (dh13 [rows,2h])
+ *   dxs = dH1 . w1[e]^T + dH3 . w3[e]^T                           (dxs [rows,d])
+ *   dw1[e] = xs_e^T . dH1,  dw3[e] = xs_e^T . dH3                (dw1, dw3 [E,d,h])
+ *   dw2[e] = act_e^T . dye_e                                      (dw2 [E,h,d])
+ * with H1, H3 from the forward's h13 and act from its act.  Weight gradients
+ * are written (not accumulated); experts with no rows get zeros.  The weight
+ * gradients have the input dtype (bf16 rounds once from fp32 sums).
+ * Same offsets and limits as xmoe_expert_ffn_up.
+ */
+xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, const void *w2,
+                                const void *act, const void *h13, const void *dye,
+                                xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                                int64_t rows, int32_t d, int32_t h, void *dh13, void *dxs,
+                                void *dw1, void *dw3, void *dw2, void *stream);
+
+/*
+ * Backward of the dispatch (the transpose of the gather):
+ *   dx[t] = sum_{j=0..k-1} dxs[slot_to_row[t*k+j]]  (+ dx_add[t])
+ * summed in fp32 in slot order, rounded once; no atomics.  dx_add [T,d] may be
+ * NULL (the shared experts' input gradient goes here).
+ */
+xmoe_status xmoe_dispatch_bwd(const void *dxs, const xmoe_pft *pft, int64_t T, int32_t d,
+                              int32_t k, xmoe_dtype dtype, const void *dx_add, void *dx,
+                              void *stream);
+
+/* Workspace bytes xmoe_route_bwd needs (0 if invalid). */
+size_t xmoe_route_bwd_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype dtype);
+
+/*
+ * Backward of the gate through the probabilities (the top-k selection is
+ * piecewise constant and carries no gradient; the biases get none):
+ *   p = softmax(logits[t]),  g[t,e] = dtopk_w[t,j] if e == topk_ids[t,j] else 0
+ *   c_t = sum_j p[t, topk_ids[t,j]] * dtopk_w[t,j]
+ *   dz[t,e] = p[t,e] * (g[t,e] - c_t) * inv_temperature
+ *   dx[t] += dz[t] . wg^T        (read-modify-write of dx [T,d])
+ *   dwg = x^T . dz               (fp32 [d,E], fixed-order split-T sum)
+ * With XMOE_BF16, dz is rounded to bf16 for the two matrix-core products
+ * (fp32 accumulation).  workspace: device, >= xmoe_route_bwd_workspace_size.
+ */
+xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits,
+                           const int32_t *topk_ids, const float *dtopk_w, xmoe_dtype dtype,
+                           int64_t T, int32_t d, int32_t E, int32_t k, float inv_temperature,
+                           void *dx, float *dwg, void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XMOE_H_ */

@@ -156,7 +156,7 @@ def ffn(xs, row_expert, w1, w3, w2, row_token=None, want_hidden: bool = False):
 
 def ffn_bwd(xs, row_expert, w1, w3, w2, dye, row_token=None, want_dh: bool = False,
             want_dw: bool = True):
-    """Backward of the SwiGLU experts.  Returns dict(dxs, dw1, dw3, dw2, [dh1, dh3])."""
+    """Backward of the SwiGLU experts.  Returns dict(dxs, dw1, dw3, dw2, [dh1, dh3, da])."""
     xs = _c(xs)
     re_ = _c(row_expert, np.int32)
     rt = _c(row_token, np.int32)
@@ -167,18 +167,19 @@ def ffn_bwd(xs, row_expert, w1, w3, w2, dye, row_token=None, want_dh: bool = Fal
     dxs = np.empty((rows, d), np.float64)
     dh1 = np.empty((rows, h), np.float64) if want_dh else None
     dh3 = np.empty((rows, h), np.float64) if want_dh else None
+    da = np.empty((rows, h), np.float64) if want_dh else None
     dw1 = np.empty((E, d, h), np.float64) if want_dw else None
     dw3 = np.empty((E, d, h), np.float64) if want_dw else None
     dw2 = np.empty((E, h, d), np.float64) if want_dw else None
     rc = lib().orc_ffn_bwd(_p(xs), I32(_dt(xs)), _p(rt), _p(re_), I64(rows), I32(d), I32(h), I32(E),
                            _p(w1), _p(w3), _p(w2), I32(_dt(w1)), _p(dye), I32(_dt(dye)), _p(dxs),
-                           _p(dh1), _p(dh3), _p(dw1), _p(dw3), _p(dw2))
+                           _p(dh1), _p(dh3), _p(da), _p(dw1), _p(dw3), _p(dw2))
     _check(rc, "ffn_bwd")
     out = {"dxs": dxs}
     if want_dw:
         out.update(dw1=dw1, dw3=dw3, dw2=dw2)
     if want_dh:
-        out.update(dh1=dh1, dh3=dh3)
+        out.update(dh1=dh1, dh3=dh3, da=da)
     return out
 
 
@@ -275,10 +276,13 @@ def _shared_slices(s1, s3, s2, n_shared: int):
 
 
 def layer_forward(inp: Dict[str, np.ndarray], k: int, mode: int, inv_tau: float = 1.0,
-                  n_shared: int = 0, tokens: Optional[np.ndarray] = None):
+                  n_shared: int = 0, tokens: Optional[np.ndarray] = None,
+                  expert_subset: Optional[np.ndarray] = None):
     """Forward of the whole layer for every token (or only `tokens`).
 
     Y[t] = sum_{j} p[t, S_t(j)] * FFN_{S_t(j)}(X[t]) + sum_s FFN^shared_s(X[t]).
+    With expert_subset (sorted expert ids), inp's w1/w3/w2 hold only those
+    experts, in that order; every routed expert must be in the subset.
     Returns a dict with the routing, the per-slot expert outputs and y."""
     x = inp["x"]
     if tokens is not None:
@@ -287,17 +291,26 @@ def layer_forward(inp: Dict[str, np.ndarray], k: int, mode: int, inv_tau: float 
     r = route(x, inp["wg"], k, mode, inv_tau, inp.get("logit_bias"), inp.get("select_bias"))
     row_token = np.repeat(np.arange(T, dtype=np.int32), k)
     row_expert = r["topk_ids"].reshape(-1)
+    if expert_subset is not None:
+        sub = np.asarray(expert_subset)
+        pos = np.searchsorted(sub, row_expert)
+        if (pos >= sub.size).any() or (sub[np.minimum(pos, sub.size - 1)] != row_expert).any():
+            raise OracleError("a token routes to an expert outside expert_subset")
+        row_expert = pos.astype(np.int32)
     row_w = r["topk_w"].reshape(-1)
-    f = ffn(x, row_expert, inp["w1"], inp["w3"], inp["w2"], row_token=row_token)
+    f = ffn(x, row_expert, inp["w1"], inp["w3"], inp["w2"], row_token=row_token, want_hidden=True)
     ysh = None
+    sh = []
     if n_shared:
         ysh = np.zeros((T, x.shape[1]), np.float64)
         zeros = np.zeros(T, np.int32)
         for (a, b, c) in _shared_slices(inp["s1"], inp["s3"], inp["s2"], n_shared):
-            ysh += ffn(x, zeros, a, b, c)["ye"]
+            g = ffn(x, zeros, a, b, c, want_hidden=True)
+            ysh += g["ye"]
+            sh.append(g)
     y = combine(f["ye"], row_token, row_w, T, y_add=ysh)
     return {"x": x, "route": r, "row_token": row_token, "row_expert": row_expert, "row_w": row_w,
-            "ye": f["ye"], "ysh": ysh, "y": y}
+            "ye": f["ye"], "h1": f["h1"], "h3": f["h3"], "act": f["act"], "ysh": ysh, "shared": sh, "y": y}
 
 
 def layer_backward(inp: Dict[str, np.ndarray], fwd: Dict, dy: np.ndarray, inv_tau: float = 1.0,
@@ -309,22 +322,23 @@ def layer_backward(inp: Dict[str, np.ndarray], fwd: Dict, dy: np.ndarray, inv_ta
     T = x.shape[0]
     cb = combine_bwd(dy, fwd["ye"], fwd["row_token"], fwd["row_w"])
     fb = ffn_bwd(x, fwd["row_expert"], inp["w1"], inp["w3"], inp["w2"], cb["dye"],
-                 row_token=fwd["row_token"], want_dw=want_dw)
+                 row_token=fwd["row_token"], want_dw=want_dw, want_dh=True)
     dx_sh = None
     sh_grads = []
     if n_shared:
         dx_sh = np.zeros_like(x, dtype=np.float64)
         zeros = np.zeros(T, np.int32)
         for (a, b, c) in _shared_slices(inp["s1"], inp["s3"], inp["s2"], n_shared):
-            g = ffn_bwd(x, zeros, a, b, c, dy, want_dw=want_dw)
+            g = ffn_bwd(x, zeros, a, b, c, dy, want_dw=want_dw, want_dh=True)
             dx_sh += g["dxs"]
             sh_grads.append(g)
     dx_moe = scatter_add(fb["dxs"], fwd["row_token"], T, dx_add=dx_sh)
     k = fwd["route"]["topk_ids"].shape[1]
     rb = route_bwd(fwd["route"]["scores"], fwd["route"]["topk_ids"], cb["dw"].reshape(T, k), x,
                    inp["wg"], inv_tau)
-    out = {"dye": cb["dye"], "dtopk_w": cb["dw"].reshape(T, k), "dxs": fb["dxs"],
-           "dx_moe": dx_moe, "dx": dx_moe + rb["dx"], "dz": rb["dz"], "dwg": rb["dwg"]}
+    out = {"dye": cb["dye"], "dtopk_w": cb["dw"].reshape(T, k), "dxs": fb["dxs"], "da": fb["da"],
+           "dh1": fb["dh1"], "dh3": fb["dh3"], "dx_moe": dx_moe, "dx": dx_moe + rb["dx"], "dz": rb["dz"],
+           "dwg": rb["dwg"], "shared": sh_grads}
     if want_dw:
         out.update(dw1=fb["dw1"], dw3=fb["dw3"], dw2=fb["dw2"])
         if n_shared:

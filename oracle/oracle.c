@@ -399,13 +399,13 @@ int orc_ffn(const void *xs, int xs_dt, const int32_t *row_token, const int32_t *
  * with H1, H3, A recomputed in double.  Weight gradients are accumulated over
  * the expert's rows in ascending row order; an expert with no rows gets an
  * explicit zero gradient.  dw1/dw3 [E,d,h], dw2 [E,h,d], dxs [rows,d];
- * dh1/dh3 [rows,h] optional.  Each expert's rows are handled by one thread, so
+ * dh1/dh3/da [rows,h] optional.  Each expert's rows are handled by one thread, so
  * the weight-gradient sums need no reduction across threads.
  */
 int orc_ffn_bwd(const void *xs, int xs_dt, const int32_t *row_token, const int32_t *row_expert,
                 int64_t rows, int d, int h, int E, const void *w1, const void *w3, const void *w2,
                 int w_dt, const void *dye, int dye_dt, double *dxs, double *dh1_out, double *dh3_out,
-                double *dw1, double *dw3, double *dw2) {
+                double *da_out, double *dw1, double *dw3, double *dw2) {
     if (!xs || !row_expert || !w1 || !w3 || !w2 || !dye || d < 1 || h < 1 || E < 1) return ORC_EINVAL;
     orc_item *items = NULL;
     int64_t *rowbuf = NULL;
@@ -462,6 +462,7 @@ int orc_ffn_bwd(const void *xs, int xs_dt, const int32_t *row_token, const int32
                         if (dxs) memcpy(dxs + r * d, DX, sizeof(double) * (size_t)d);
                         if (dh1_out) memcpy(dh1_out + r * h, D1, sizeof(double) * (size_t)h);
                         if (dh3_out) memcpy(dh3_out + r * h, D3, sizeof(double) * (size_t)h);
+                        if (da_out) memcpy(da_out + r * h, DA, sizeof(double) * (size_t)h);
                         if (dw1 || dw3)
                             for (int i = 0; i < d; ++i) {
                                 double *p1 = dw1 ? dw1 + ((int64_t)e * d + i) * h : NULL;

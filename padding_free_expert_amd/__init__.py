@@ -1,0 +1,237 @@
+"""Padding-free MoE layer for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of libxmoe.so (the C ABI in include/xmoe.h): the same entry
+points under the same names, taking torch tensors that already live on the GPU.
+The binding only marshals arguments -- pointers, sizes, the current HIP stream
+-- and every step of the layer runs in the library's HIP kernels.  There is no
+CPU or PyTorch fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "XmoeError", "PFT", "lib_path", "xmoe_version", "xmoe_query_device", "xmoe_route",
+    "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn_up",
+    "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_combine", "xmoe_combine_bwd",
+    "xmoe_expert_ffn_bwd", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILE = os.path.join(_HERE, "libxmoe.so")
+
+if not os.path.exists(_LIB_FILE):
+    raise ImportError(f"{_LIB_FILE} is not built; run __graft_entry__.build() (or "
+                      f"python padding_free_expert_amd/build.py) first")
+
+_lib = ctypes.CDLL(_LIB_FILE)
+
+XMOE_F32, XMOE_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid value", 2: "unsupported", 3: "workspace", 4: "hip error"}
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class _CPft(ctypes.Structure):
+    _fields_ = [("token_ids", _vp), ("expert_ids", _vp), ("tokens_per_expert", _vp),
+                ("expert_offsets", _vp), ("combine_weights", _vp), ("slot_to_row", _vp)]
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_lib_last_error = _sig("xmoe_last_error", [], ctypes.c_char_p)
+_lib_version = _sig("xmoe_version", [])
+_lib_query = _sig("xmoe_query_device", [ctypes.c_int, ctypes.POINTER(ctypes.c_int)])
+_lib_route = _sig("xmoe_route", [_vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
+                                 _vp, _vp])
+_lib_pft_ws = _sig("xmoe_build_pft_workspace_size", [_i64, _i32, _i32], _sz)
+_lib_pft = _sig("xmoe_build_pft", [_vp, _vp, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _sz, _vp])
+_lib_dispatch = _sig("xmoe_dispatch", [_vp, ctypes.c_int, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _vp])
+_lib_up = _sig("xmoe_expert_ffn_up", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp])
+_lib_down = _sig("xmoe_expert_ffn_down", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+_lib_ffn = _sig("xmoe_expert_ffn", [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp,
+                                    _vp, _vp])
+_lib_combine = _sig("xmoe_combine", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp])
+_lib_combine_bwd = _sig("xmoe_combine_bwd", [_vp, _vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int,
+                                             _vp, _vp, _vp])
+_lib_ffn_bwd = _sig("xmoe_expert_ffn_bwd", [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64,
+                                            _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp])
+_lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp,
+                                               _vp, _vp])
+_lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
+_lib_rbwd = _sig("xmoe_route_bwd", [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp,
+                                    _vp, _vp, _sz, _vp])
+
+
+class XmoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise XmoeError(st, where)
+
+
+def lib_path() -> str:
+    return _LIB_FILE
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libxmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libxmoe takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return XMOE_BF16
+    if t.dtype == torch.float32:
+        return XMOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class PFT:
+    """Device tensors of the Padding-Free Token buffer for T tokens, E experts, top-k."""
+
+    def __init__(self, T: int, E: int, k: int, device="cuda"):
+        R = T * k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.T, self.E, self.k = T, E, k
+        self.token_ids = torch.empty(R, **i32)
+        self.expert_ids = torch.empty(R, **i32)
+        self.tokens_per_expert = torch.empty(E, **i32)
+        self.expert_offsets = torch.empty(E + 1, **i32)
+        self.combine_weights = torch.empty(R, dtype=torch.float32, device=device)
+        self.slot_to_row = torch.empty(R, **i32)
+
+    def c(self) -> _CPft:
+        return _CPft(_ptr(self.token_ids), _ptr(self.expert_ids), _ptr(self.tokens_per_expert),
+                     _ptr(self.expert_offsets), _ptr(self.combine_weights), _ptr(self.slot_to_row))
+
+    def fields(self):
+        return {"token_ids": self.token_ids, "expert_ids": self.expert_ids,
+                "tokens_per_expert": self.tokens_per_expert, "expert_offsets": self.expert_offsets,
+                "combine_weights": self.combine_weights, "slot_to_row": self.slot_to_row}
+
+
+def xmoe_version() -> int:
+    return int(_lib_version())
+
+
+def xmoe_query_device(ordinal: int = 0) -> bool:
+    v = ctypes.c_int(0)
+    _check(_lib_query(ordinal, ctypes.byref(v)), "xmoe_query_device")
+    return bool(v.value)
+
+
+def xmoe_route(x, wg, k: int, topk_ids, topk_w, logits, inv_temperature: float = 1.0,
+               logit_bias=None, select_bias=None, stream=None):
+    T, d = x.shape
+    E = wg.shape[1]
+    _check(_lib_route(_ptr(x), _ptr(wg), _dt(x), T, d, E, k, inv_temperature, _ptr(logit_bias),
+                      _ptr(select_bias), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _stream(stream)),
+           "xmoe_route")
+
+
+def xmoe_build_pft_workspace_size(T: int, E: int, k: int) -> int:
+    return int(_lib_pft_ws(T, E, k))
+
+
+def xmoe_build_pft(topk_ids, topk_w, E: int, pft: PFT, workspace, stream=None):
+    T, k = topk_ids.shape
+    c = pft.c()
+    _check(_lib_pft(_ptr(topk_ids), _ptr(topk_w), T, E, k, ctypes.byref(c), _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_build_pft")
+
+
+def xmoe_dispatch(x, k: int, pft: PFT, xs, stream=None):
+    T, d = x.shape
+    c = pft.c()
+    _check(_lib_dispatch(_ptr(x), _dt(x), T, d, k, ctypes.byref(c), _ptr(xs), _stream(stream)),
+           "xmoe_dispatch")
+
+
+def xmoe_expert_ffn_up(xs, w1, w3, expert_offsets, act, h13=None, stream=None):
+    rows, d = xs.shape
+    E, _, h = w1.shape
+    _check(_lib_up(_ptr(xs), _ptr(w1), _ptr(w3), _dt(xs), _ptr(expert_offsets), E, rows, d, h, _ptr(act),
+                   _ptr(h13), _stream(stream)), "xmoe_expert_ffn_up")
+
+
+def xmoe_expert_ffn_down(act, w2, expert_offsets, ye, stream=None):
+    rows, h = act.shape
+    E, _, d = w2.shape
+    _check(_lib_down(_ptr(act), _ptr(w2), _dt(act), _ptr(expert_offsets), E, rows, d, h, _ptr(ye),
+                     _stream(stream)), "xmoe_expert_ffn_down")
+
+
+def xmoe_expert_ffn(xs, w1, w3, w2, expert_offsets, act, ye, h13=None, stream=None):
+    rows, d = xs.shape
+    E, _, h = w1.shape
+    _check(_lib_ffn(_ptr(xs), _ptr(w1), _ptr(w3), _ptr(w2), _dt(xs), _ptr(expert_offsets), E, rows, d, h,
+                    _ptr(act), _ptr(h13), _ptr(ye), _stream(stream)), "xmoe_expert_ffn")
+
+
+def xmoe_combine(ye, pft: PFT, T: int, y, y_add=None, stream=None):
+    d = ye.shape[1]
+    c = pft.c()
+    _check(_lib_combine(_ptr(ye), ctypes.byref(c), T, d, pft.k, _dt(ye), _ptr(y_add), _ptr(y), _stream(stream)),
+           "xmoe_combine")
+
+
+def xmoe_combine_bwd(dy, ye, pft: PFT, dye, dtopk_w, stream=None):
+    T, d = dy.shape
+    c = pft.c()
+    _check(_lib_combine_bwd(_ptr(dy), _ptr(ye), ctypes.byref(c), T, d, pft.k, _dt(dy), _ptr(dye), _ptr(dtopk_w),
+                            _stream(stream)), "xmoe_combine_bwd")
+
+
+def xmoe_expert_ffn_bwd(xs, w1, w3, w2, act, h13, dye, expert_offsets, dh13, dxs, dw1, dw3, dw2, stream=None):
+    rows, d = xs.shape
+    E, _, h = w1.shape
+    _check(_lib_ffn_bwd(_ptr(xs), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(act), _ptr(h13), _ptr(dye), _dt(xs),
+                        _ptr(expert_offsets), E, rows, d, h, _ptr(dh13), _ptr(dxs), _ptr(dw1), _ptr(dw3),
+                        _ptr(dw2), _stream(stream)), "xmoe_expert_ffn_bwd")
+
+
+def xmoe_dispatch_bwd(dxs, pft: PFT, T: int, dx, dx_add=None, stream=None):
+    d = dxs.shape[1]
+    c = pft.c()
+    _check(_lib_dispatch_bwd(_ptr(dxs), ctypes.byref(c), T, d, pft.k, _dt(dxs), _ptr(dx_add), _ptr(dx),
+                             _stream(stream)), "xmoe_dispatch_bwd")
+
+
+def xmoe_route_bwd_workspace_size(T: int, d: int, E: int, dtype: torch.dtype) -> int:
+    return int(_lib_rbwd_ws(T, d, E, XMOE_BF16 if dtype == torch.bfloat16 else XMOE_F32))
+
+
+def xmoe_route_bwd(x, wg, logits, topk_ids, dtopk_w, dx, dwg, workspace, inv_temperature: float = 1.0,
+                   stream=None):
+    T, d = x.shape
+    E = wg.shape[1]
+    k = topk_ids.shape[1]
+    _check(_lib_rbwd(_ptr(x), _ptr(wg), _ptr(logits), _ptr(topk_ids), _ptr(dtopk_w), _dt(x), T, d, E, k,
+                     inv_temperature, _ptr(dx), _ptr(dwg), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_route_bwd")

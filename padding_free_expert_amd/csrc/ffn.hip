@@ -1,0 +1,161 @@
+// Expert FFN forward and backward on the expert-sorted (padding-free) rows.
+//
+// X-MoE article (adg.csdn.net), section 2.1.2 "跨平台核函数优化": the experts'
+// GEMMs take each expert's rows as a dynamic slice -- no padding to a common
+// capacity -- where the article's sketch loops over the experts on the host.
+// Here one launch covers every expert: the grid is sized from the row count
+// and the expert count, and each block finds its expert and row tile from the
+// device-side offsets (see gemm.hpp).  The expert is a SwiGLU FFN (a reading:
+// the pages name no FFN form), so the up-projection multiplies the same rows
+// by W1 and W3 in one kernel and applies silu(H1) * H3 in its epilogue.
+//
+// Products (rows of expert e = [off[e], off[e+1]); weights row-major):
+//   up       act = silu(xs.W1) * (xs.W3)        A = xs, B = W1 | W3 (n-contiguous)
+//   down     ye  = act.W2                       A = act, B = W2 (n-contiguous)
+//   dgrad2   dA  = dye.W2^T -> dH1, dH3         A = dye, B = W2 read k-contiguous
+//   dgrad1   dxs = dH1.W1^T + dH3.W3^T          two k phases, B read k-contiguous
+//   wgrad13  dW1 = xs^T dH1, dW3 = xs^T dH3     reduction over the expert's rows
+//   wgrad2   dW2 = act^T dye                    reduction over the expert's rows
+#include "common.hpp"
+#include "gemm.hpp"
+#include "kernels.hpp"
+
+namespace xmoe {
+
+namespace {
+
+GemmArgs rows_args(const int32_t *offsets, int E, int64_t rows) {
+    GemmArgs p{};
+    p.group_mode = GM_ROWS;
+    p.offsets = offsets;
+    p.G = E;
+    p.extent = rows;
+    p.nphase = 1;
+    return p;
+}
+
+GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
+    GemmArgs p{};
+    p.group_mode = GM_KSPLIT;
+    p.offsets = offsets;
+    p.G = E;
+    p.extent = rows;
+    p.nphase = 1;
+    return p;
+}
+
+}  // namespace
+
+hipError_t launch_ffn_up(int dt, const void *xs, const void *w1, const void *w3, const int32_t *offsets, int E,
+                         int64_t rows, int d, int h, void *act, void *h13, hipStream_t s) {
+    GemmArgs p = rows_args(offsets, E, rows);
+    p.N = h;
+    p.K = d;
+    p.A0 = xs;
+    p.lda = d;
+    p.B0 = w1;
+    p.Bx = w3;
+    p.ldb = h;
+    p.b_gstride = static_cast<int64_t>(d) * h;
+    p.C0 = act;
+    p.ldc = h;
+    p.aux_out = h13;
+    p.ld_aux = 2 * static_cast<int64_t>(h);
+    p.hoff = h;
+    return dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 2, true, false, EPI_SWIGLU, bf16_t>(p, s)
+                       : launch_gemm_f32<2, true, false, EPI_SWIGLU>(p, s);
+}
+
+hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows, int d,
+                           int h, void *ye, hipStream_t s) {
+    GemmArgs p = rows_args(offsets, E, rows);
+    p.N = d;
+    p.K = h;
+    p.A0 = act;
+    p.lda = h;
+    p.B0 = w2;
+    p.ldb = d;
+    p.b_gstride = static_cast<int64_t>(h) * d;
+    p.C0 = ye;
+    p.ldc = d;
+    return dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, false, EPI_STORE, bf16_t>(p, s)
+                       : launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
+}
+
+hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
+                          const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d, int h,
+                          void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s) {
+    const int64_t dh = static_cast<int64_t>(d) * h;
+    const size_t esz = dt == kBF16 ? 2 : 4;
+    hipError_t err;
+    {   // dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13
+        GemmArgs p = rows_args(offsets, E, rows);
+        p.N = h;
+        p.K = d;
+        p.A0 = dye;
+        p.lda = d;
+        p.B0 = w2;          // B(k=c, n=j) = W2[e][j*d + c]
+        p.ldb = d;
+        p.b_gstride = dh;
+        p.C0 = dh13;
+        p.ldc = 2 * static_cast<int64_t>(h);
+        p.aux = h13;
+        p.ld_aux = 2 * static_cast<int64_t>(h);
+        p.hoff = h;
+        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_SWIGLU_BWD, bf16_t>(p, s)
+                          : launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s);
+        if (err != hipSuccess) return err;
+    }
+    {   // dxs = dH1 . W1[e]^T + dH3 . W3[e]^T
+        GemmArgs p = rows_args(offsets, E, rows);
+        p.N = d;
+        p.K = h;
+        p.nphase = 2;
+        p.A0 = dh13;
+        p.A1 = static_cast<const char *>(dh13) + h * esz;
+        p.lda = 2 * static_cast<int64_t>(h);
+        p.B0 = w1;          // B(k=j, n=i) = W1[e][i*h + j]
+        p.B1 = w3;
+        p.ldb = h;
+        p.b_gstride = dh;
+        p.C0 = dxs;
+        p.ldc = d;
+        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_STORE, bf16_t>(p, s)
+                          : launch_gemm_f32<1, true, true, EPI_STORE>(p, s);
+        if (err != hipSuccess) return err;
+    }
+    {   // dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert)
+        GemmArgs p = ksplit_args(offsets, E, rows);
+        p.M = d;
+        p.N = h;
+        p.A0 = xs;          // A(m=i, k=r) = xs[r*d + i]
+        p.lda = d;
+        p.B0 = dh13;        // B(k=r, n=j) = dh13[r*2h + j]
+        p.Bx = static_cast<const char *>(dh13) + h * esz;
+        p.ldb = 2 * static_cast<int64_t>(h);
+        p.C0 = dw1;
+        p.Cx = dw3;
+        p.ldc = h;
+        p.c_gstride = dh;
+        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 2, false, false, EPI_STORE, bf16_t>(p, s)
+                          : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
+        if (err != hipSuccess) return err;
+    }
+    {   // dW2[e] = act_e^T . dye_e
+        GemmArgs p = ksplit_args(offsets, E, rows);
+        p.M = h;
+        p.N = d;
+        p.A0 = act;         // A(m=j, k=r) = act[r*h + j]
+        p.lda = h;
+        p.B0 = dye;         // B(k=r, n=c) = dye[r*d + c]
+        p.ldb = d;
+        p.C0 = dw2;
+        p.ldc = d;
+        p.c_gstride = dh;
+        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, false, false, EPI_STORE, bf16_t>(p, s)
+                          : launch_gemm_f32<1, false, false, EPI_STORE>(p, s);
+    }
+    return err;
+}
+
+}  // namespace xmoe

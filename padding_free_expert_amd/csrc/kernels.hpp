@@ -1,0 +1,52 @@
+// Internal launchers of libxmoe (C++ linkage; the C ABI lives in api.cpp).
+// Each launcher enqueues its kernels on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xmoe {
+
+// dtype tags as in the C ABI
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+struct PftPtrs {
+    int32_t *token_ids, *expert_ids, *tokens_per_expert, *expert_offsets;
+    float *combine_weights;
+    int32_t *slot_to_row;
+};
+
+// router
+hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d, int E, int k, float inv_tau,
+                        const float *logit_bias, const float *select_bias, int32_t *topk_ids, float *topk_w,
+                        float *logits, hipStream_t s);
+size_t route_bwd_workspace(int64_t T, int d, int E, int dt);
+hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
+                            const float *dtopk_w, int64_t T, int d, int E, int k, float inv_tau, void *dx,
+                            float *dwg, void *ws, hipStream_t s);
+
+// Padding-Free Token buffer
+size_t pft_workspace(int64_t T, int E);
+hipError_t launch_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k,
+                            const PftPtrs &pft, void *ws, hipStream_t s);
+
+// row movement
+hipError_t launch_dispatch(int dt, const void *x, const int32_t *slot_to_row, int64_t T, int d, int k, void *xs,
+                           hipStream_t s);
+hipError_t launch_gather_sum(int dt, const void *src, const int32_t *slot_to_row, const float *weights, int64_t T,
+                             int d, int k, const void *add, void *out, hipStream_t s);
+hipError_t launch_combine_bwd(int dt, const void *dy, const void *ye, const int32_t *slot_to_row,
+                              const float *weights, int64_t T, int d, int k, void *dye, float *dtopk_w,
+                              hipStream_t s);
+
+// expert FFN
+hipError_t launch_ffn_up(int dt, const void *xs, const void *w1, const void *w3, const int32_t *offsets, int E,
+                         int64_t rows, int d, int h, void *act, void *h13, hipStream_t s);
+hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows,
+                           int d, int h, void *ye, hipStream_t s);
+hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
+                          const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d,
+                          int h, void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s);
+
+}  // namespace xmoe

@@ -1,0 +1,148 @@
+// Padding-Free Token buffer construction.
+//
+// X-MoE article (adg.csdn.net), section 2.1.1 "PFT数据结构创新": instead of
+// fixed-capacity expert buffers, a compact buffer records, per routed
+// (token, expert) pair, the token's position, the expert, the combine weight
+// and the per-expert token counts -- nothing padded, nothing dropped.  The
+// row order is the one the article's per-expert GEMM (section 2.1.2) visits:
+// experts ascending, tokens in input order within an expert.
+//
+// Three kernels, no host synchronisation and no global atomics:
+//   1. count:   each block takes 256 consecutive tokens and marks, in an LDS
+//               bitmap of E x 256 bits, which of its tokens chose each expert;
+//               the popcount of an expert's 256 bits is the block's count.
+//   2. scan:    one block turns the [blocks x E] counts into tokens_per_expert,
+//               the exclusive scan expert_offsets, and each block's first row
+//               per expert.
+//   3. scatter: each block rebuilds its bitmap; the row of (t, e) is the
+//               block's base for e plus the number of lower tokens of the block
+//               whose bit for e is set -- a stable (expert, token) order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace xmoe {
+
+namespace {
+
+constexpr int kChunk = 256;          // tokens per block
+constexpr int kWords = kChunk / 32;  // bitmap words per expert
+constexpr int kMaxE = 1024;
+
+__device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int64_t T, int E, int k) {
+    for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) bm[i] = 0u;
+    __syncthreads();
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
+    if (t < T) {
+        const uint32_t bit = 1u << (threadIdx.x & 31);
+        const int w = threadIdx.x >> 5;
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[t * k + j];
+            if (e >= 0 && e < E) atomicOr(&bm[e * kWords + w], bit);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
+                                                        int32_t *__restrict__ counts) {
+    __shared__ uint32_t bm[kMaxE * kWords];
+    build_bitmap(bm, ids, T, E, k);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) c += __popc(bm[e * kWords + w]);
+        counts[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+    }
+}
+
+// One block of 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restrict__ counts, int nblk, int E,
+                                                        int32_t *__restrict__ base, int32_t *__restrict__ tpe,
+                                                        int32_t *__restrict__ offsets) {
+    __shared__ int wave_tot[16];
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E)
+        for (int b = 0; b < nblk; ++b) {
+            const int64_t i = static_cast<int64_t>(b) * E + e;
+            base[i] = total;
+            total += counts[i];
+        }
+    // exclusive scan of `total` over e: within each wave, then across waves
+    const int lane = e & 63, wv = e >> 6;
+    int inc = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += v;
+    }
+    if (lane == 63) wave_tot[wv] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += wave_tot[w];
+    const int off_e = before + inc - total;
+    if (e < E) {
+        tpe[e] = total;
+        offsets[e] = off_e;
+        if (e == E - 1) offsets[E] = off_e + total;
+        for (int b = 0; b < nblk; ++b) base[static_cast<int64_t>(b) * E + e] += off_e;
+    }
+}
+
+__global__ __launch_bounds__(256) void pft_scatter_kernel(const int32_t *__restrict__ ids,
+                                                          const float *__restrict__ wt, int64_t T, int E, int k,
+                                                          const int32_t *__restrict__ base, int32_t *__restrict__ tok,
+                                                          int32_t *__restrict__ eid, float *__restrict__ cw,
+                                                          int32_t *__restrict__ s2r) {
+    __shared__ uint32_t bm[kMaxE * kWords];
+    build_bitmap(bm, ids, T, E, k);
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
+    if (t >= T) return;
+    const int64_t R = T * k;
+    const int wd = threadIdx.x >> 5;
+    const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
+    for (int j = 0; j < k; ++j) {
+        const int e = ids[t * k + j];
+        int64_t r = -1;
+        if (e >= 0 && e < E) {
+            int rank = __popc(bm[e * kWords + wd] & below);
+            for (int q = 0; q < wd; ++q) rank += __popc(bm[e * kWords + q]);
+            r = base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+            if (r >= R) r = -1;
+        }
+        s2r[t * k + j] = static_cast<int32_t>(r);
+        if (r >= 0) {
+            if (tok) tok[r] = static_cast<int32_t>(t);
+            if (eid) eid[r] = e;
+            if (cw) cw[r] = wt ? wt[t * k + j] : 0.0f;
+        }
+    }
+}
+
+}  // namespace
+
+size_t pft_workspace(int64_t T, int E) {
+    const int64_t nblk = (T + kChunk - 1) / kChunk;
+    return static_cast<size_t>(2 * nblk * E) * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, const PftPtrs &pft, void *ws,
+                            hipStream_t s) {
+    const int64_t nblk = (T + kChunk - 1) / kChunk;
+    int32_t *counts = static_cast<int32_t *>(ws);
+    int32_t *base = counts + nblk * E;
+    if (nblk > 0) {
+        hipLaunchKernelGGL(pft_count_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, counts);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(pft_scan_kernel, dim3(1), dim3(1024), 0, s, counts, static_cast<int>(nblk), E, base,
+                       pft.tokens_per_expert, pft.expert_offsets);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || nblk == 0) return err;
+    hipLaunchKernelGGL(pft_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, base,
+                       pft.token_ids, pft.expert_ids, pft.combine_weights, pft.slot_to_row);
+    return hipGetLastError();
+}
+
+}  // namespace xmoe

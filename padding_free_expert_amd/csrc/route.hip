@@ -1,0 +1,281 @@
+// Router (gate) forward and backward.
+//
+// "5.4 MoE模型在分布式训练中的应用", section 训练流程: every device computes the
+// gate scores of its own tokens; X-MoE notes "略读笔记90", section 需求:
+// fine-grained experts are used with a large top-k.  The pages give no gate
+// formula; the one implemented is a softmax over the E experts of
+// s = (x . Wg) * inv_tau + logit_bias, the top-k of s + select_bias with ties to
+// the lower expert index, and the chosen probabilities as (unrenormalised)
+// combine weights.
+//
+// Forward: one product x . Wg whose epilogue applies the scale and bias and
+// stores the fp32 scores, then one wavefront per token for softmax + top-k
+// (k rounds of a wavefront-wide arg-max under the order (sel desc, index asc)).
+// Backward: one wavefront per token forms dz = p * (g - c) * inv_tau; two
+// products then give dx += dz . Wg^T and the split-T partials of Wg's gradient,
+// which a last kernel sums in a fixed order.
+#include <algorithm>
+
+#include "common.hpp"
+#include "gemm.hpp"
+#include "kernels.hpp"
+
+namespace xmoe {
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int Q>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ logits,
+                                                           const float *__restrict__ sbias, int64_t T, int E, int k,
+                                                           int32_t *__restrict__ ids, float *__restrict__ w) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    float s[Q], sel[Q];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        s[q] = -INFINITY;
+        sel[q] = -INFINITY;
+        if (e < E) {
+            s[q] = logits[t * E + e];
+            sel[q] = sbias ? __fadd_rn(s[q], sbias[e]) : s[q];
+            mx = fmaxf(mx, s[q]);
+        }
+    }
+    mx = wave_max(mx);
+    float den = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (lane + 64 * q < E) den += expf(s[q] - mx);
+    den = wave_sum(den);
+    uint32_t taken = 0u;
+    for (int j = 0; j < k; ++j) {
+        float bv = 0.0f;
+        int bi = 0x7fffffff;  // no candidate
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int e = lane + 64 * q;
+            if (e < E && !((taken >> q) & 1u) && (bi == 0x7fffffff || sel[q] > bv)) {
+                bv = sel[q];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (lane == (bi & 63)) {
+            const int qb = bi >> 6;
+            float sb = 0.0f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                if (q == qb) sb = s[q];
+            taken |= 1u << qb;
+            ids[t * k + j] = bi;
+            w[t * k + j] = expf(sb - mx) / den;
+        }
+    }
+}
+
+template <int Q, typename OutT>
+__global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__ logits,
+                                                       const int32_t *__restrict__ ids,
+                                                       const float *__restrict__ dw, int64_t T, int E, int k,
+                                                       float inv_tau, OutT *__restrict__ dz) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    float p[Q], g[Q];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        p[q] = -INFINITY;
+        g[q] = 0.0f;
+        if (e < E) {
+            p[q] = logits[t * E + e];
+            mx = fmaxf(mx, p[q]);
+        }
+    }
+    mx = wave_max(mx);
+    float den = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        p[q] = (lane + 64 * q < E) ? expf(p[q] - mx) : 0.0f;
+        den += p[q];
+    }
+    den = wave_sum(den);
+    for (int j = 0; j < k; ++j) {
+        const int ej = ids[t * k + j];
+        const float gj = dw[t * k + j];
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (lane + 64 * q == ej) g[q] = gj;
+    }
+    float c = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        p[q] /= den;
+        c += p[q] * g[q];
+    }
+    c = wave_sum(c);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int e = lane + 64 * q;
+        if (e < E) Elem<OutT>::store(dz, t * E + e, p[q] * (g[q] - c) * inv_tau);
+    }
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restrict__ part, int S, int64_t n,
+                                                           float *__restrict__ out) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) acc += part[s * n + i];
+        out[i] = acc;
+    }
+}
+
+inline int q_of(int E) {
+    const int q = (E + 63) / 64;
+    return q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : 16;
+}
+
+// split count of the reduction over tokens for Wg's gradient: enough blocks to
+// fill the chip, at least 1024 tokens per split
+inline int rbwd_splits(int64_t T, int d, int E) {
+    const int64_t tiles = ((d + 127) / 128) * ((E + 63) / 64);
+    int64_t S = (512 + tiles - 1) / tiles;
+    const int64_t maxS = (T + 1023) / 1024;
+    if (S > maxS) S = maxS;
+    if (S < 1) S = 1;
+    if (S > 64) S = 64;
+    return static_cast<int>(S);
+}
+
+inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d, int E, int k, float inv_tau,
+                        const float *logit_bias, const float *select_bias, int32_t *topk_ids, float *topk_w,
+                        float *logits, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    GemmArgs p{};
+    p.group_mode = GM_ROWS;
+    p.offsets = nullptr;
+    p.G = 1;
+    p.extent = T;
+    p.kchunk = static_cast<int>(T);
+    p.N = E;
+    p.K = d;
+    p.nphase = 1;
+    p.A0 = x;
+    p.lda = d;
+    p.B0 = wg;
+    p.ldb = E;
+    p.C0 = logits;
+    p.ldc = E;
+    p.scale = inv_tau;
+    p.col_bias = logit_bias;
+    hipError_t err = dt == kBF16 ? launch_gemm_mfma<128, 64, 64, 4, 1, 1, true, false, EPI_ROUTER, float>(p, s)
+                                 : launch_gemm_f32<1, true, false, EPI_ROUTER>(p, s);
+    if (err != hipSuccess) return err;
+    const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves)), block(256);
+    switch (q_of(E)) {
+        case 1: hipLaunchKernelGGL(topk_softmax_kernel<1>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+        case 2: hipLaunchKernelGGL(topk_softmax_kernel<2>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+        case 4: hipLaunchKernelGGL(topk_softmax_kernel<4>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+        case 8: hipLaunchKernelGGL(topk_softmax_kernel<8>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+        default: hipLaunchKernelGGL(topk_softmax_kernel<16>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+    }
+    return hipGetLastError();
+}
+
+size_t route_bwd_workspace(int64_t T, int d, int E, int dt) {
+    const int S = rbwd_splits(T, d, E);
+    const size_t dz = align256(static_cast<size_t>(T) * E * (dt == kBF16 ? 2 : 4));
+    const size_t part = align256(static_cast<size_t>(S) * d * E * 4);
+    return dz + part;
+}
+
+template <typename OutT>
+static void launch_dz(int E, dim3 grid, hipStream_t s, const float *logits, const int32_t *ids, const float *dw,
+                      int64_t T, int k, float inv_tau, OutT *dz) {
+    switch (q_of(E)) {
+        case 1: hipLaunchKernelGGL((route_dz_kernel<1, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+        case 2: hipLaunchKernelGGL((route_dz_kernel<2, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+        case 4: hipLaunchKernelGGL((route_dz_kernel<4, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+        case 8: hipLaunchKernelGGL((route_dz_kernel<8, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+        default: hipLaunchKernelGGL((route_dz_kernel<16, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+    }
+}
+
+hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
+                            const float *dtopk_w, int64_t T, int d, int E, int k, float inv_tau, void *dx,
+                            float *dwg, void *ws, hipStream_t s) {
+    const int S = rbwd_splits(T, d, E);
+    const size_t dz_bytes = align256(static_cast<size_t>(T) * E * (dt == kBF16 ? 2 : 4));
+    void *dz = ws;
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + dz_bytes);
+    hipError_t err;
+    if (T > 0) {
+        const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves));
+        if (dt == kBF16) launch_dz<bf16_t>(E, grid, s, logits, topk_ids, dtopk_w, T, k, inv_tau, static_cast<bf16_t *>(dz));
+        else launch_dz<float>(E, grid, s, logits, topk_ids, dtopk_w, T, k, inv_tau, static_cast<float *>(dz));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+
+        // dx[t] += dz[t] . Wg^T : A = dz [T,E] (k-contiguous), B(k=e, n=i) = Wg[i*E + e]
+        GemmArgs a{};
+        a.group_mode = GM_ROWS;
+        a.G = 1;
+        a.extent = T;
+        a.kchunk = static_cast<int>(T);
+        a.N = d;
+        a.K = E;
+        a.nphase = 1;
+        a.A0 = dz;
+        a.lda = E;
+        a.B0 = wg;
+        a.ldb = E;
+        a.C0 = dx;
+        a.ldc = d;
+        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_ACCUM, bf16_t>(a, s)
+                          : launch_gemm_f32<1, true, true, EPI_ACCUM>(a, s);
+        if (err != hipSuccess) return err;
+    }
+    // partial[s] = x[chunk s]^T . dz[chunk s] : A(m=i, k=t) = x[t*d + i], B(k=t, n=e) = dz[t*E + e]
+    GemmArgs b{};
+    b.group_mode = GM_KSPLIT;
+    b.offsets = nullptr;
+    b.G = S;
+    b.extent = T;
+    b.kchunk = static_cast<int>((T + S - 1) / S);
+    b.M = d;
+    b.N = E;
+    b.nphase = 1;
+    b.A0 = x;
+    b.lda = d;
+    b.B0 = dz;
+    b.ldb = E;
+    b.C0 = part;
+    b.ldc = E;
+    b.c_gstride = static_cast<int64_t>(d) * E;
+    err = dt == kBF16 ? launch_gemm_mfma<128, 64, 64, 2, 2, 1, false, false, EPI_STORE, float>(b, s)
+                      : launch_gemm_f32<1, false, false, EPI_STORE>(b, s);
+    if (err != hipSuccess) return err;
+    const int64_t n = static_cast<int64_t>(d) * E;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096));
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(blocks), dim3(256), 0, s, part, S, n, dwg);
+    return hipGetLastError();
+}
+
+}  // namespace xmoe

@@ -1,0 +1,136 @@
+"""A padding-free MoE layer driven through libxmoe.
+
+Owns every buffer of one layer invocation (allocated once, with torch, on the
+GPU) and runs the forward and backward as the sequence of C-ABI calls the
+X-MoE pages describe ("5.4 MoE模型在分布式训练中的应用", section 训练流程: gate,
+dispatch, experts, combine, then the reverse path).  No arithmetic happens in
+Python: every step is a libxmoe kernel.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import (PFT, xmoe_build_pft, xmoe_build_pft_workspace_size, xmoe_combine, xmoe_combine_bwd,
+               xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_route,
+               xmoe_route_bwd, xmoe_route_bwd_workspace_size)
+
+
+class PaddingFreeMoE:
+    """Buffers and call sequence for one layer of T tokens.
+
+    weights: dict with wg [d,E], w1/w3 [E,d,h], w2 [E,h,d]; optional shared-expert
+    weights s1/s3 [d, n*h_s], s2 [n*h_s, d] (the shared experts side by side),
+    logit_bias / select_bias fp32 [E]."""
+
+    def __init__(self, weights: Dict[str, torch.Tensor], T: int, k: int, inv_tau: float = 1.0,
+                 backward: bool = True):
+        self.w = weights
+        wg, w1 = weights["wg"], weights["w1"]
+        self.dtype = wg.dtype
+        self.device = wg.device
+        self.T, self.k, self.inv_tau = T, k, inv_tau
+        self.d, self.E = wg.shape
+        self.h = w1.shape[2]
+        self.shared = weights.get("s1") is not None
+        self.backward_enabled = backward
+        dev, dt = self.device, self.dtype
+        T, d, E, h, R = T, self.d, self.E, self.h, T * k
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), **f32)
+        self.logits = torch.empty((T, E), **f32)
+        self.pft = PFT(T, E, k, dev)
+        self.pft_ws = torch.empty(max(xmoe_build_pft_workspace_size(T, E, k), 16), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty((R, d), dtype=dt, device=dev)
+        self.act = torch.empty((R, h), dtype=dt, device=dev)
+        self.h13 = torch.empty((R, 2 * h), dtype=dt, device=dev) if backward else None
+        self.ye = torch.empty((R, d), dtype=dt, device=dev)
+        self.y = torch.empty((T, d), dtype=dt, device=dev)
+        if self.shared:
+            hs = weights["s1"].shape[1]
+            self.hs = hs
+            self.sh_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+            self.sh_act = torch.empty((T, hs), dtype=dt, device=dev)
+            self.sh_h13 = torch.empty((T, 2 * hs), dtype=dt, device=dev) if backward else None
+            self.sh_y = torch.empty((T, d), dtype=dt, device=dev)
+        if backward:
+            self.dtopk_w = torch.empty((T, k), **f32)
+            self.dye = torch.empty((R, d), dtype=dt, device=dev)
+            self.dh13 = torch.empty((R, 2 * h), dtype=dt, device=dev)
+            self.dxs = torch.empty((R, d), dtype=dt, device=dev)
+            self.dw1 = torch.empty((E, d, h), dtype=dt, device=dev)
+            self.dw3 = torch.empty((E, d, h), dtype=dt, device=dev)
+            self.dw2 = torch.empty((E, h, d), dtype=dt, device=dev)
+            self.dx = torch.empty((T, d), dtype=dt, device=dev)
+            self.dwg = torch.empty((d, E), **f32)
+            self.rbwd_ws = torch.empty(max(xmoe_route_bwd_workspace_size(T, d, E, dt), 16), dtype=torch.uint8,
+                                       device=dev)
+            if self.shared:
+                hs = self.hs
+                self.sh_dh13 = torch.empty((T, 2 * hs), dtype=dt, device=dev)
+                self.sh_dx = torch.empty((T, d), dtype=dt, device=dev)
+                self.ds1 = torch.empty((1, d, hs), dtype=dt, device=dev)
+                self.ds3 = torch.empty((1, d, hs), dtype=dt, device=dev)
+                self.ds2 = torch.empty((1, hs, d), dtype=dt, device=dev)
+
+    # views of the shared-expert weights as a single expert of width n*h_s
+    def _shared_w(self):
+        w = self.w
+        return w["s1"].unsqueeze(0), w["s3"].unsqueeze(0), w["s2"].unsqueeze(0)
+
+    def forward(self, x: torch.Tensor, stream=None, hook=None) -> torch.Tensor:
+        """hook(name), if given, is called after each library call is enqueued."""
+        w = self.w
+        mark = hook or (lambda name: None)
+        xmoe_route(x, w["wg"], self.k, self.topk_ids, self.topk_w, self.logits, self.inv_tau,
+                   w.get("logit_bias"), w.get("select_bias"), stream=stream)
+        mark("route")
+        xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=stream)
+        mark("build_pft")
+        xmoe_dispatch(x, self.k, self.pft, self.xs, stream=stream)
+        mark("dispatch")
+        xmoe_expert_ffn(self.xs, w["w1"], w["w3"], w["w2"], self.pft.expert_offsets, self.act, self.ye,
+                        h13=self.h13, stream=stream)
+        mark("expert_ffn")
+        y_add = None
+        if self.shared:
+            s1, s3, s2 = self._shared_w()
+            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y, h13=self.sh_h13, stream=stream)
+            mark("shared_ffn")
+            y_add = self.sh_y
+        xmoe_combine(self.ye, self.pft, self.T, self.y, y_add=y_add, stream=stream)
+        mark("combine")
+        self.x = x
+        return self.y
+
+    def backward(self, dy: torch.Tensor, stream=None, hook=None) -> torch.Tensor:
+        w = self.w
+        mark = hook or (lambda name: None)
+        xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w, stream=stream)
+        mark("combine_bwd")
+        xmoe_expert_ffn_bwd(self.xs, w["w1"], w["w3"], w["w2"], self.act, self.h13, self.dye,
+                            self.pft.expert_offsets, self.dh13, self.dxs, self.dw1, self.dw3, self.dw2,
+                            stream=stream)
+        mark("expert_ffn_bwd")
+        dx_add = None
+        if self.shared:
+            s1, s3, s2 = self._shared_w()
+            xmoe_expert_ffn_bwd(self.x, s1, s3, s2, self.sh_act, self.sh_h13, dy, self.sh_off, self.sh_dh13,
+                                self.sh_dx, self.ds1, self.ds3, self.ds2, stream=stream)
+            mark("shared_ffn_bwd")
+            dx_add = self.sh_dx
+        xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=stream)
+        mark("dispatch_bwd")
+        xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.dx, self.dwg,
+                       self.rbwd_ws, self.inv_tau, stream=stream)
+        mark("route_bwd")
+        return self.dx
+
+    def grads(self) -> Dict[str, torch.Tensor]:
+        g = {"dx": self.dx, "dwg": self.dwg, "dw1": self.dw1, "dw3": self.dw3, "dw2": self.dw2,
+             "dtopk_w": self.dtopk_w, "dye": self.dye, "dxs": self.dxs, "dh13": self.dh13}
+        if self.shared:
+            g.update(ds1=self.ds1[0], ds3=self.ds3[0], ds2=self.ds2[0])
+        return g

@@ -1,0 +1,143 @@
+"""Shared test helpers: comparison to the oracle under the stated tolerances.
+
+Tolerance (one reading for every floating-point output): normwise
+||g - r||_2 <= rtol * ||r||_2 and elementwise |g - r| <= rtol * (|r| + floor),
+with rtol = 1e-4 for fp32 workloads and 2e-2 for bf16 workloads (an fp64 oracle
+on the identical bf16 inputs).  The floor is rms(r) for outputs computed
+element by element.  For outputs that are sums over rows (weight gradients
+c_ij = sum_r a_ri b_rj) it is the root-sum-square of the summed terms,
+sqrt(sum_r (a_ri b_rj)^2), taken from the oracle's fp64 factors: each term
+carries the rounding of its bf16 factors, so that is the scale of the sum's
+error, and a sum whose terms cancel has no meaningful relative error of its
+own.  The floor keeps entries near zero from producing meaningless relative
+errors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+RTOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """GPU/CPU tensor -> float64 (floats) or int array on the host."""
+    t = t.detach().cpu()
+    if t.dtype in (torch.int32, torch.int64):
+        return t.numpy()
+    return t.to(torch.float64).numpy()
+
+
+def orc_in(t: torch.Tensor) -> np.ndarray:
+    """Tensor -> oracle input: bf16 as uint16 bit patterns, fp32 as float32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.int32:
+        return t.numpy()
+    raise TypeError(t.dtype)
+
+
+def rss_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """sqrt(sum_r (a[r,i] * b[r,j])^2): the scale of c = a^T b's rounding error."""
+    return np.sqrt(np.maximum((a * a).T @ (b * b), 0.0))
+
+
+def assert_close(got, ref, rtol: float, name: str = "", floor=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    if ref.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    lim = rtol * (np.abs(ref) + (rms if floor is None else np.asarray(floor, np.float64)))
+    bad = err > lim
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - lim), err.shape)
+        fl = rms if floor is None else float(np.broadcast_to(floor, err.shape)[i])
+        raise AssertionError(f"{name}: {int(bad.sum())}/{err.size} elements beyond tolerance; worst at {i}: "
+                             f"got {got[i]!r} ref {ref[i]!r} (floor {fl:.3e}, rms {rms:.3e}, rtol {rtol})")
+    nrm = float(np.linalg.norm(ref))
+    if nrm > 0:
+        rel = float(np.linalg.norm(got - ref)) / nrm
+        assert rel <= rtol, f"{name}: normwise relative error {rel:.3e} > {rtol}"
+
+
+def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias, k: int, score_tol: float):
+    """Compare the GPU's top-k with the oracle's.
+
+    Both sides decide in fp32 on their own logits; the GPU's logits may differ
+    from the oracle's by rounding.  With delta = 2 * max |s_gpu - s_oracle|
+    (checked against score_tol), a token whose top-(k+1) fp32 selection keys
+    are all more than delta apart has one correct answer and must match
+    exactly; for the others any choice consistent within delta is correct and
+    is checked for validity.  Returns the boolean mask of tokens whose GPU
+    expert set differs from the oracle's."""
+    s_orc = orc["scores"]
+    T, E = s_orc.shape
+    diff = float(np.max(np.abs(gpu_logits - s_orc))) if s_orc.size else 0.0
+    scale = float(np.max(np.abs(s_orc))) if s_orc.size else 1.0
+    assert diff <= score_tol * max(scale, 1.0), f"router scores differ by {diff:.3e}"
+    sel = s_orc.astype(np.float32)
+    if select_bias is not None:
+        sel = (sel + np.asarray(select_bias, np.float32)).astype(np.float32)
+    sel = sel.astype(np.float64)
+    # two fp32 roundings of the bias add may also differ by an ulp
+    delta = 2.0 * diff + 4.0 * np.finfo(np.float32).eps * max(float(np.max(np.abs(sel))), 1.0)
+    order = np.argsort(-sel, axis=1, kind="stable")
+    top = np.take_along_axis(sel, order[:, :min(k + 1, E)], 1)
+    gaps = -np.diff(top, axis=1)
+    ambiguous = (gaps.min(axis=1) <= delta) if gaps.shape[1] else np.zeros(T, bool)
+    oid = orc["topk_ids"]
+    clear = ~ambiguous
+    np.testing.assert_array_equal(gpu_ids[clear], oid[clear])
+    mismatch = np.zeros(T, bool)
+    for t in np.nonzero(ambiguous)[0]:
+        g = gpu_ids[t]
+        assert len(set(g.tolist())) == k and g.min() >= 0 and g.max() < E
+        kth = sel[t, order[t, k - 1]]
+        nxt = sel[t, order[t, k]] if k < E else -np.inf
+        gs = sel[t, g]
+        assert (gs >= kth - delta).all(), (t, g, gs, kth, delta)
+        must = np.nonzero(sel[t] > nxt + delta)[0]
+        assert set(must.tolist()) <= set(g.tolist()), (t, must, g)
+        assert (np.diff(gs) <= delta).all(), (t, gs)
+        mismatch[t] = set(g.tolist()) != set(oid[t].tolist())
+    return mismatch
+
+
+def swiglu_wgrad_scales(x, da, h1, h3, act, dye):
+    """Root-sum-square error scales of one expert's weight gradients.
+
+    dW1 = x^T dH1 with dH1 = dA*H3*g(H1), g(a) = sig(a)(1 + a(1 - sig(a))):
+    rounding H1 and H3 to bf16 moves dH1 by up to ~2.3 * 2^-9 * |dA*H3|
+    (|g| <= 1.1 and |a g'(a)| <= 0.13), whatever the size of dH1 itself --
+    g has a zero near a = -1.28, where dH1 vanishes but its error does not.
+    Likewise dH3 = dA*silu(H1) moves by ~|dA*H1| * 2^-9, and dW2 = act^T dYe
+    carries the rounding of act and dYe.  The scales are the root-sum-square
+    over rows of those magnitudes; all inputs are oracle (fp64) values."""
+    ad = np.abs(da)
+    return (rss_rows(x, ad * np.abs(h3)), rss_rows(x, ad * np.abs(h1)), rss_rows(act, dye))
+
+
+def assert_wgrad_close(got, ref, rows_of, floors_of, rtol: float, name: str):
+    """Per-expert weight gradient: normwise per expert that has rows,
+    elementwise with the given per-expert floor, exact zeros for experts
+    without rows.  rows_of(e) -> number of rows; floors_of(e) -> floor array."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    for e in range(ref.shape[0]):
+        if rows_of(e) == 0:
+            assert (got[e] == 0).all(), f"{name}[{e}]: expert without rows must get a zero gradient"
+            continue
+        assert_close(got[e], ref[e], rtol, f"{name}[{e}]", floor=floors_of(e))

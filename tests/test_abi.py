@@ -1,0 +1,69 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, answers the workspace queries, and rejects invalid arguments
+on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "xmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xmoe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def xm():
+    import padding_free_expert_amd as m
+    return m
+
+
+def test_header_declares_the_layer_calls():
+    names = _declared()
+    for n in ["xmoe_route", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn", "xmoe_combine",
+              "xmoe_combine_bwd", "xmoe_expert_ffn_bwd", "xmoe_dispatch_bwd", "xmoe_route_bwd"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(xm):
+    lib = ctypes.CDLL(xm.lib_path())
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_workspace_queries(xm):
+    import torch
+    assert xm.xmoe_build_pft_workspace_size(32768, 160, 8) >= 2 * 128 * 160 * 4
+    assert xm.xmoe_build_pft_workspace_size(0, 8, 2) > 0
+    assert xm.xmoe_build_pft_workspace_size(10, 8, 9) == 0          # k > E
+    assert xm.xmoe_build_pft_workspace_size(10, 2000, 2) == 0       # E > 1024
+    assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 64, torch.bfloat16) >= 4096 * 64 * 2
+    assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 0, torch.bfloat16) == 0
+
+
+def test_invalid_arguments_rejected_on_host(xm):
+    lib = xm._lib
+    # xmoe_route with NULL pointers
+    assert xm._lib_route(None, None, 1, 10, 8, 8, 2, 1.0, None, None, None, None, None, None) == 1
+    assert b"NULL" in xm._lib_last_error()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails before any use
+    # k > E
+    assert xm._lib_route(p, p, 1, 10, 8, 8, 9, 1.0, None, None, p, p, p, None) == 1
+    # unknown dtype
+    assert xm._lib_route(p, p, 7, 10, 8, 8, 2, 1.0, None, None, p, p, p, None) == 2
+    # bf16 with d not a multiple of 8
+    assert xm._lib_route(p, p, 1, 10, 12, 8, 2, 1.0, None, None, p, p, p, None) == 2
+    # expert FFN: h not a multiple of 8, E out of range, NULL offsets
+    assert xm._lib_up(p, p, p, 1, p, 4, 100, 64, 12, p, None, None) == 2
+    assert xm._lib_up(p, p, p, 1, p, 0, 100, 64, 64, p, None, None) == 1
+    assert xm._lib_up(p, p, p, 1, None, 4, 100, 64, 64, p, None, None) == 1
+    # build_pft: workspace too small
+    pft = xm._CPft(16, 16, 16, 16, 16, 16)
+    assert xm._lib_pft(p, p, 1000, 16, 4, ctypes.byref(pft), p, 8, None) == 3
+    # dispatch: T*k overflow
+    assert lib.xmoe_dispatch(p, 1, ctypes.c_int64(1 << 30), 64, 8, ctypes.byref(pft), p, None) == 1
+    assert xm._lib_last_error() != b""

@@ -1,0 +1,308 @@
+"""Per-step GPU parity: each libxmoe entry point against the CPU oracle on the
+same seeded generator inputs (never on another GPU step's output).
+
+Integer work (routing indices, the Padding-Free Token buffer, the dispatch copy)
+must match bit for bit; floating-point outputs must meet the tolerance of
+_helpers.assert_close.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import workloads
+from _helpers import (RTOL, assert_close, assert_wgrad_close, host, need_gpu, orc_in, routing_check, rss_rows,
+                      swiglu_wgrad_scales)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def xm():
+    need_gpu()
+    import padding_free_expert_amd as m
+    assert m.xmoe_query_device(0), "device 0 is not gfx950"
+    return m
+
+
+def _gpu_pft(xm, ids, w, E):
+    T, k = ids.shape
+    pft = xm.PFT(T, E, k)
+    ws = torch.empty(max(xm.xmoe_build_pft_workspace_size(T, E, k), 16), dtype=torch.uint8, device="cuda")
+    xm.xmoe_build_pft(ids.cuda(), w.cuda(), E, pft, ws)
+    torch.cuda.synchronize()
+    return pft
+
+
+# ------------------------------------------------------------------ routing
+
+def test_router_fp32_is_bit_exact(xm):
+    """fp32 path: one fused multiply-add per feature in ascending order on both
+    sides -> identical logits and identical selections, tie-break included."""
+    wl = workloads.get("tiny_f32")
+    inp = workloads.generate(wl, experts=False)
+    x, wg = inp["x"], inp["wg"]
+    T, E, k = wl.T, wl.E, wl.k
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    xm.xmoe_route(x.cuda(), wg.cuda(), k, ids, w, lg)
+    r = orc.route(orc_in(x), orc_in(wg), k, 0)
+    np.testing.assert_array_equal(host(lg), r["scores"])
+    np.testing.assert_array_equal(host(ids), r["topk_ids"])
+    assert_close(host(w), r["topk_w"], 1e-5, "topk_w")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_exact_grid_ties(xm, dtype):
+    """Inputs on a coarse binary grid: every logit is exact in any summation
+    order, so the matrix-core path must match bit for bit, ties included."""
+    T, d, E, k = 300, 64, 16, 4
+    x, wg = workloads.exact_router_inputs(T, d, E, seed=5)
+    x, wg = x.to(DT[dtype]), wg.to(DT[dtype])
+    sb = torch.zeros(E)
+    sb[3] = 0.25
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    xm.xmoe_route(x.cuda(), wg.cuda(), k, ids, w, lg, 2.0, None, sb.cuda())
+    r = orc.route(orc_in(x), orc_in(wg), k, 1, 2.0, None, sb.numpy())
+    np.testing.assert_array_equal(host(lg), r["scores"])
+    np.testing.assert_array_equal(host(ids), r["topk_ids"])
+    assert_close(host(w), r["topk_w"], 1e-5, "topk_w")
+
+
+@pytest.mark.parametrize("name", ["dsmoe16b", "dsv3", "zipf_skew", "long_batch"])
+def test_router_bf16_small(xm, name):
+    wl = workloads.small(name)
+    inp = workloads.generate(wl, experts=False, backward=False)
+    T, E, k = wl.T, wl.E, wl.k
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    lb, sb = inp["logit_bias"], inp["select_bias"]
+    xm.xmoe_route(inp["x"].cuda(), inp["wg"].cuda(), k, ids, w, lg, wl.inv_tau,
+                  None if lb is None else lb.cuda(), None if sb is None else sb.cuda())
+    r = orc.route(orc_in(inp["x"]), orc_in(inp["wg"]), k, 1, wl.inv_tau,
+                  None if lb is None else lb.numpy(), None if sb is None else sb.numpy())
+    mism = routing_check(host(ids), host(lg), r, None if sb is None else sb.numpy(), k, 1e-5)
+    keep = ~mism
+    ok = (host(ids) == r["topk_ids"]).all(axis=1) & keep
+    assert_close(host(w)[ok], r["topk_w"][ok], 1e-4, "topk_w")
+
+
+# ------------------------------------------------------------------ PFT
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 8, 2, 0.0), (255, 8, 2, 0.0), (256, 64, 6, 0.0), (257, 64, 6, 0.0),
+                                        (1000, 128, 8, 2.5), (3000, 160, 8, 0.0), (700, 1024, 16, 1.0),
+                                        (64, 8, 8, 0.0), (32768, 160, 8, 0.0), (16384, 128, 8, 3.0)])
+def test_build_pft_bit_exact(xm, T, E, k, skew):
+    ids, w = workloads.random_topk(T, E, k, seed=T * 7 + E, skew=skew)
+    pft = _gpu_pft(xm, ids, w, E)
+    ref = orc.build_pft(ids.numpy(), w.numpy(), E)
+    for key, t in pft.fields().items():
+        got = t.cpu().numpy()
+        if key == "combine_weights":
+            np.testing.assert_array_equal(got.view(np.uint32), ref[key].view(np.uint32), err_msg=key)
+        else:
+            np.testing.assert_array_equal(got, ref[key], err_msg=key)
+
+
+def test_build_pft_zero_tokens(xm):
+    E, k = 16, 4
+    pft = xm.PFT(0, E, k)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    ids = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    xm.xmoe_build_pft(ids, w, E, pft, ws)
+    torch.cuda.synchronize()
+    assert (pft.tokens_per_expert.cpu() == 0).all() and (pft.expert_offsets.cpu() == 0).all()
+
+
+# ------------------------------------------------------------------ dispatch / combine
+
+@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 16, 6), ("f32", 256, 128, 8, 2),
+                                           ("bf16", 1, 2048, 64, 6), ("bf16", 4096, 7168, 256, 8)])
+def test_dispatch_exact(xm, dtype, T, d, E, k):
+    ids, w = workloads.random_topk(T, E, k, seed=3)
+    x = workloads.random_rows(T, d, dtype, seed=4)
+    pft = _gpu_pft(xm, ids, w, E)
+    xs = torch.empty((T * k, d), dtype=DT[dtype], device="cuda")
+    xm.xmoe_dispatch(x.cuda(), k, pft, xs)
+    ref = orc.build_pft(ids.numpy(), w.numpy(), E)
+    got = xs.cpu()
+    want = orc.gather(orc_in(x), ref["token_ids"])
+    np.testing.assert_array_equal(got.to(torch.float64).numpy(), want)
+
+
+@pytest.mark.parametrize("dtype,T,d,E,k,with_add", [("bf16", 300, 256, 16, 6, True), ("f32", 256, 128, 8, 2, False),
+                                                    ("bf16", 777, 520, 40, 8, False), ("bf16", 2, 64, 8, 8, True)])
+def test_combine(xm, dtype, T, d, E, k, with_add):
+    ids, w = workloads.random_topk(T, E, k, seed=11)
+    pft = _gpu_pft(xm, ids, w, E)
+    ye = workloads.random_rows(T * k, d, dtype, seed=12)
+    add = workloads.random_rows(T, d, dtype, seed=13) if with_add else None
+    y = torch.empty((T, d), dtype=DT[dtype], device="cuda")
+    xm.xmoe_combine(ye.cuda(), pft, T, y, y_add=None if add is None else add.cuda())
+    ref = orc.build_pft(ids.numpy(), w.numpy(), E)
+    want = orc.combine(host(ye), ref["token_ids"], ref["combine_weights"].astype(np.float64), T,
+                       y_add=None if add is None else orc_in(add))
+    assert_close(host(y), want, RTOL[dtype] if dtype == "bf16" else 1e-5, "y")
+
+
+@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 16, 6), ("f32", 256, 128, 8, 2), ("bf16", 513, 2048, 64, 6)])
+def test_combine_bwd(xm, dtype, T, d, E, k):
+    ids, w = workloads.random_topk(T, E, k, seed=21)
+    pft = _gpu_pft(xm, ids, w, E)
+    ye = workloads.random_rows(T * k, d, dtype, seed=22)
+    dy = workloads.random_rows(T, d, dtype, seed=23)
+    dye = torch.empty((T * k, d), dtype=DT[dtype], device="cuda")
+    dtw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    xm.xmoe_combine_bwd(dy.cuda(), ye.cuda(), pft, dye, dtw)
+    ref = orc.build_pft(ids.numpy(), w.numpy(), E)
+    g = orc.combine_bwd(orc_in(dy), host(ye), ref["token_ids"], ref["combine_weights"].astype(np.float64))
+    assert_close(host(dye), g["dye"], RTOL[dtype] if dtype == "bf16" else 1e-6, "dye")
+    dw_slot = g["dw"][ref["slot_to_row"]].reshape(T, k)
+    assert_close(host(dtw), dw_slot, 1e-4, "dtopk_w")
+
+
+@pytest.mark.parametrize("dtype,T,d,E,k,with_add", [("bf16", 300, 256, 16, 6, True), ("f32", 256, 128, 8, 2, True),
+                                                    ("bf16", 1000, 1024, 128, 8, False)])
+def test_dispatch_bwd(xm, dtype, T, d, E, k, with_add):
+    ids, w = workloads.random_topk(T, E, k, seed=31)
+    pft = _gpu_pft(xm, ids, w, E)
+    dxs = workloads.random_rows(T * k, d, dtype, seed=32)
+    add = workloads.random_rows(T, d, dtype, seed=33) if with_add else None
+    dx = torch.empty((T, d), dtype=DT[dtype], device="cuda")
+    xm.xmoe_dispatch_bwd(dxs.cuda(), pft, T, dx, dx_add=None if add is None else add.cuda())
+    ref = orc.build_pft(ids.numpy(), w.numpy(), E)
+    want = orc.scatter_add(orc_in(dxs), ref["token_ids"], T, dx_add=None if add is None else orc_in(add))
+    assert_close(host(dx), want, RTOL[dtype] if dtype == "bf16" else 1e-6, "dx")
+
+
+# ------------------------------------------------------------------ expert FFN
+
+FFN_CASES = [
+    # dtype, rows, d, h, E, empty_frac
+    ("f32", 512, 128, 64, 8, 0.0),
+    ("f32", 301, 64, 40, 5, 0.4),
+    ("bf16", 700, 256, 200, 16, 0.25),
+    ("bf16", 1030, 448, 136, 32, 0.5),
+    ("bf16", 129, 128, 128, 1, 0.0),
+    ("bf16", 3000, 512, 384, 4, 0.0),
+]
+
+
+def _ffn_inputs(dtype, rows, d, h, E, empty, seed):
+    off = workloads.random_segments(rows, E, seed=seed, empty_frac=empty)
+    xs = workloads.random_rows(rows, d, dtype, seed=seed + 1)
+    g = torch.Generator().manual_seed(seed)
+    tdt = DT[dtype]
+    w1 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w3 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w2 = (torch.randn((E, h, d), generator=g) / h ** 0.5).to(tdt)
+    re_ = np.repeat(np.arange(E, dtype=np.int32), np.diff(off.numpy()))
+    return off, xs, w1, w3, w2, re_
+
+
+@pytest.mark.parametrize("dtype,rows,d,h,E,empty", FFN_CASES)
+def test_expert_ffn_forward(xm, dtype, rows, d, h, E, empty):
+    off, xs, w1, w3, w2, re_ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=rows + d)
+    tdt = DT[dtype]
+    act = torch.empty((rows, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((rows, 2 * h), dtype=tdt, device="cuda")
+    ye = torch.empty((rows, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn(xs.cuda(), w1.cuda(), w3.cuda(), w2.cuda(), off.cuda(), act, ye, h13=h13)
+    ref = orc.ffn(orc_in(xs), re_, orc_in(w1), orc_in(w3), orc_in(w2), want_hidden=True)
+    rt = RTOL[dtype]
+    hh = host(h13)
+    assert_close(hh[:, :h], ref["h1"], rt, "h1")
+    assert_close(hh[:, h:], ref["h3"], rt, "h3")
+    assert_close(host(act), ref["act"], rt, "act")
+    assert_close(host(ye), ref["ye"], rt, "ye")
+
+
+@pytest.mark.parametrize("dtype,rows,d,h,E,empty", FFN_CASES)
+def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
+    off, xs, w1, w3, w2, re_ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=rows + 2 * d)
+    tdt = DT[dtype]
+    dye = workloads.random_rows(rows, d, dtype, seed=rows + 5)
+    c = lambda t: t.cuda()
+    act = torch.empty((rows, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((rows, 2 * h), dtype=tdt, device="cuda")
+    ye = torch.empty((rows, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn(c(xs), c(w1), c(w3), c(w2), c(off), act, ye, h13=h13)
+    dh13 = torch.empty((rows, 2 * h), dtype=tdt, device="cuda")
+    dxs = torch.empty((rows, d), dtype=tdt, device="cuda")
+    dw1 = torch.full((E, d, h), float("nan"), dtype=tdt, device="cuda")   # must be fully overwritten
+    dw3 = torch.full((E, d, h), float("nan"), dtype=tdt, device="cuda")
+    dw2 = torch.full((E, h, d), float("nan"), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_bwd(c(xs), c(w1), c(w3), c(w2), act, h13, c(dye), c(off), dh13, dxs, dw1, dw3, dw2)
+    ref = orc.ffn_bwd(orc_in(xs), re_, orc_in(w1), orc_in(w3), orc_in(w2), orc_in(dye), want_dh=True)
+    fwd = orc.ffn(orc_in(xs), re_, orc_in(w1), orc_in(w3), orc_in(w2), want_hidden=True)
+    rt = RTOL[dtype]
+    g = host(dh13)
+    assert_close(g[:, :h], ref["dh1"], rt, "dh1")
+    assert_close(g[:, h:], ref["dh3"], rt, "dh3")
+    assert_close(host(dxs), ref["dxs"], rt, "dxs")
+    o = off.numpy()
+    X, G = host(xs), host(dye)
+    scales = {}
+
+    def floors(e):
+        if e not in scales:
+            sl = slice(o[e], o[e + 1])
+            scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl], G[sl])
+        return scales[e]
+
+    rows = lambda e: o[e + 1] - o[e]
+    assert_wgrad_close(host(dw1), ref["dw1"], rows, lambda e: floors(e)[0], rt, "dw1")
+    assert_wgrad_close(host(dw3), ref["dw3"], rows, lambda e: floors(e)[1], rt, "dw3")
+    assert_wgrad_close(host(dw2), ref["dw2"], rows, lambda e: floors(e)[2], rt, "dw2")
+
+
+# ------------------------------------------------------------------ router backward
+
+@pytest.mark.parametrize("dtype,T,d,E,k,inv_tau", [("f32", 256, 128, 8, 2, 1.0), ("bf16", 300, 256, 16, 6, 1.0),
+                                                   ("bf16", 2500, 512, 160, 8, 2.0), ("bf16", 777, 448, 64, 6, 1.0)])
+def test_route_bwd(xm, dtype, T, d, E, k, inv_tau):
+    tdt = DT[dtype]
+    g = torch.Generator().manual_seed(T + E)
+    x = workloads.random_rows(T, d, dtype, seed=41)
+    wg = (torch.randn((d, E), generator=g) / d ** 0.5).to(tdt)
+    logits = torch.randn((T, E), generator=g) * 2.0
+    ids, _ = workloads.random_topk(T, E, k, seed=42)
+    dtw = torch.randn((T, k), generator=g)
+    dx0 = workloads.random_rows(T, d, dtype, seed=43)
+    dx = dx0.cuda().clone()
+    dwg = torch.empty((d, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(xm.xmoe_route_bwd_workspace_size(T, d, E, tdt), dtype=torch.uint8, device="cuda")
+    xm.xmoe_route_bwd(x.cuda(), wg.cuda(), logits.cuda(), ids.cuda(), dtw.cuda(), dx, dwg, ws, inv_tau)
+    ref = orc.route_bwd(logits.numpy().astype(np.float64), ids.numpy(), dtw.numpy().astype(np.float64),
+                        orc_in(x), orc_in(wg), inv_tau)
+    rt = RTOL[dtype]
+    assert_close(host(dx), host(dx0) + ref["dx"], rt, "dx")
+    assert_close(host(dwg), ref["dwg"], rt, "dwg", floor=rss_rows(host(x), ref["dz"]))
+
+
+# ------------------------------------------------------------------ error paths on the device
+
+def test_rejects_bad_arguments_without_launching(xm):
+    x = torch.zeros((8, 12), dtype=torch.bfloat16, device="cuda")   # d = 12: not a multiple of 8
+    wg = torch.zeros((12, 8), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((8, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((8, 2), dtype=torch.float32, device="cuda")
+    lg = torch.empty((8, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(xm.XmoeError) as e:
+        xm.xmoe_route(x, wg, 2, ids, w, lg)
+    assert e.value.status == 2
+    with pytest.raises(xm.XmoeError) as e:
+        xm.xmoe_route(x[:, :8].contiguous(), wg[:8].contiguous(), 9, ids, w, lg)   # k > E
+    assert e.value.status == 1
+    pft = xm.PFT(8, 8, 2)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(xm.XmoeError) as e:
+        xm.xmoe_build_pft(ids, w, 8, pft, small_ws)
+    assert e.value.status == 3
