@@ -116,18 +116,22 @@ def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias,
     return mismatch
 
 
-def swiglu_wgrad_scales(x, da, h1, h3, act, dye):
+def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2):
     """Root-sum-square error scales of one expert's weight gradients.
 
     dW1 = x^T dH1 with dH1 = dA*H3*g(H1), g(a) = sig(a)(1 + a(1 - sig(a))):
     rounding H1 and H3 to bf16 moves dH1 by up to ~2.3 * 2^-9 * |dA*H3|
     (|g| <= 1.1 and |a g'(a)| <= 0.13), whatever the size of dH1 itself --
     g has a zero near a = -1.28, where dH1 vanishes but its error does not.
-    Likewise dH3 = dA*silu(H1) moves by ~|dA*H1| * 2^-9, and dW2 = act^T dYe
-    carries the rounding of act and dYe.  The scales are the root-sum-square
-    over rows of those magnitudes; all inputs are oracle (fp64) values."""
-    ad = np.abs(da)
-    return (rss_rows(x, ad * np.abs(h3)), rss_rows(x, ad * np.abs(h1)), rss_rows(act, dye))
+    Likewise dH3 = dA*silu(H1) moves by ~|dA*H1| * 2^-9.  dA = dYe.W2^T itself
+    carries the rounding of dYe, whose scale is the root-sum-square of the
+    terms dYe*W2 (not |dA|, which may cancel), so the magnitude used for dA is
+    |dA| + sqrt(dYe^2 . (W2^2)^T).  dW2 = act^T dYe carries the rounding of act
+    and dYe.  The scales are the root-sum-square over rows of those
+    magnitudes; every input is an oracle (fp64) value or a generator input."""
+    w2 = np.asarray(w2, np.float64)
+    dam = np.abs(da) + np.sqrt(np.maximum((dye * dye) @ (w2 * w2).T, 0.0))
+    return (rss_rows(x, dam * np.abs(h3)), rss_rows(x, dam * np.abs(h1)), rss_rows(act, dye))
 
 
 def assert_wgrad_close(got, ref, rows_of, floors_of, rtol: float, name: str):
@@ -141,3 +145,50 @@ def assert_wgrad_close(got, ref, rows_of, floors_of, rtol: float, name: str):
             assert (got[e] == 0).all(), f"{name}[{e}]: expert without rows must get a zero gradient"
             continue
         assert_close(got[e], ref[e], rtol, f"{name}[{e}]", floor=floors_of(e))
+
+
+def by_expert(ids: np.ndarray, vals: np.ndarray) -> np.ndarray:
+    """Per-slot values reordered by expert id within each token, so that two
+    routings that chose the same experts in a different slot order compare."""
+    order = np.argsort(ids, axis=1, kind="stable")
+    return np.take_along_axis(np.asarray(vals), order, 1)
+
+
+def pft_invariants(ids: np.ndarray, w: np.ndarray, E: int, pft: dict):
+    """Properties every valid Padding-Free Token buffer of routing (ids, w) has:
+    T*k rows, each token k times, each (token, expert) once, rows grouped by
+    ascending expert with tokens ascending inside a group, offsets = scan of
+    the counts, slot_to_row consistent with the routing, weights copied bit
+    for bit.  Checks a buffer against its own routing, without any oracle."""
+    T, k = ids.shape
+    R = T * k
+    tpe, off = pft["tokens_per_expert"], pft["expert_offsets"]
+    assert tpe.sum() == R and off[0] == 0 and off[-1] == R and (np.diff(off) == tpe).all()
+    assert (np.bincount(pft["token_ids"], minlength=T) == k).all()
+    assert np.unique(pft["token_ids"].astype(np.int64) * E + pft["expert_ids"]).size == R
+    assert (np.diff(pft["expert_ids"]) >= 0).all()
+    same = np.diff(pft["expert_ids"]) == 0
+    assert (np.diff(pft["token_ids"])[same] > 0).all()
+    assert (pft["expert_ids"][off[:-1][tpe > 0]] == np.nonzero(tpe > 0)[0]).all()
+    s2r = pft["slot_to_row"].reshape(T, k)
+    assert (pft["token_ids"][s2r] == np.arange(T)[:, None]).all()
+    assert (pft["expert_ids"][s2r] == ids).all()
+    np.testing.assert_array_equal(pft["combine_weights"][s2r].view(np.uint32), np.asarray(w, np.float32).view(np.uint32))
+
+
+def router_wgrad_floor(x, probs, ids, ye_slot, dy, dz, inv_tau):
+    """Error scale of dWg = x^T dz when dz comes out of the layer's own chain.
+
+    dz[t,e] = p[t,e] * (g[t,e] - c_t) * inv_tau with g the routing-weight
+    gradient <dy[t], Ye[t,j]> at the chosen experts.  Those dot products carry
+    the bf16 rounding of Ye; their error scale is G[t,j] = sqrt(sum_c
+    (dy[t,c] Ye[t,j,c])^2), which g - c may cancel but its error does not.
+    The magnitude per term is |dz| + inv_tau * p * (G + sum_j p_j G_j), and the
+    floor is its root-sum-square over tokens (oracle values throughout)."""
+    T, k = ids.shape
+    G = np.sqrt(((ye_slot.reshape(T, k, -1) * dy[:, None, :]) ** 2).sum(-1))
+    Gfull = np.zeros_like(probs)
+    np.put_along_axis(Gfull, ids, G, 1)
+    pc = (np.take_along_axis(probs, ids, 1) * G).sum(1, keepdims=True)
+    mag = np.abs(dz) + inv_tau * probs * (Gfull + pc)
+    return rss_rows(x, mag)

@@ -12,7 +12,8 @@ import torch
 
 import oracle as orc
 import workloads
-from _helpers import (RTOL, assert_close, assert_wgrad_close, host, need_gpu, orc_in, routing_check,
+from _helpers import (RTOL, assert_close, assert_wgrad_close, by_expert, host, need_gpu, orc_in, pft_invariants,
+                      router_wgrad_floor, routing_check,
                       swiglu_wgrad_scales)
 
 pytestmark = pytest.mark.gpu
@@ -74,10 +75,14 @@ def test_layer_forward_backward(xm, name):
                                   layer.topk_w.cpu().numpy())
     if not mism.any():
         ref = orc.build_pft(fwd["route"]["topk_ids"], fwd["route"]["topk_w"].astype(np.float32), wl.E)
-        for key in ("token_ids", "expert_ids", "tokens_per_expert", "expert_offsets", "slot_to_row"):
+        for key in ("token_ids", "expert_ids", "tokens_per_expert", "expert_offsets"):
             np.testing.assert_array_equal(pft[key], ref[key], err_msg=key)
+        # slots of near-tied experts may be ordered differently: compare where the order agrees
+        same = (gids == fwd["route"]["topk_ids"]).all(axis=1)
+        np.testing.assert_array_equal(pft["slot_to_row"].reshape(wl.T, wl.k)[same],
+                                      ref["slot_to_row"].reshape(wl.T, wl.k)[same])
         assert_close(pft["combine_weights"], ref["combine_weights"], 1e-5, "combine_weights")
-    assert pft["tokens_per_expert"].sum() == wl.T * wl.k
+    pft_invariants(gids, layer.topk_w.cpu().numpy(), wl.E, pft)
 
     # dispatch is an exact copy of the rows its own buffer names
     np.testing.assert_array_equal(host(layer.xs), host(inp["x"])[pft["token_ids"]])
@@ -86,13 +91,16 @@ def test_layer_forward_backward(xm, name):
     assert_close(host(layer.y)[ok], fwd["y"][ok], rt, "y")
     assert_close(host(layer.dx)[ok], bwd["dx"][ok], rt, "dx")
     # the routing weights' gradient, per slot
-    assert_close(host(layer.dtopk_w)[ok], bwd["dtopk_w"][ok], rt, "dtopk_w")
+    assert_close(by_expert(gids[ok], host(layer.dtopk_w)[ok]),
+                 by_expert(fwd["route"]["topk_ids"][ok], bwd["dtopk_w"][ok]), rt, "dtopk_w")
     X = host(inp["x"])
     if wl.n_shared:
         hs = wl.h_shared
         for s_ in range(wl.n_shared):
             f, b = fwd["shared"][s_], bwd["shared"][s_]
-            f1, f3, f2 = swiglu_wgrad_scales(X, b["da"], f["h1"], f["h3"], f["act"], host(inp["dy"]))
+            cs = slice(s_ * hs, (s_ + 1) * hs)
+            f1, f3, f2 = swiglu_wgrad_scales(X, b["da"], f["h1"], f["h3"], f["act"], host(inp["dy"]),
+                                             host(inp["s2"])[cs, :])
             cs = slice(s_ * hs, (s_ + 1) * hs)
             assert_close(host(layer.ds1[0])[:, cs], bwd["ds1"][:, cs], rt, f"ds1[{s_}]", floor=f1)
             assert_close(host(layer.ds3[0])[:, cs], bwd["ds3"][:, cs], rt, f"ds3[{s_}]", floor=f3)
@@ -109,7 +117,7 @@ def test_layer_forward_backward(xm, name):
         if e not in scales:
             r = fwd["row_expert"] == e
             scales[e] = swiglu_wgrad_scales(Xr[r], bwd["da"][r], fwd["h1"][r], fwd["h3"][r], fwd["act"][r],
-                                            bwd["dye"][r])
+                                            bwd["dye"][r], host(inp["w2"][e]))
         return scales[e]
 
     def rows(e):
@@ -123,7 +131,9 @@ def test_layer_forward_backward(xm, name):
     assert_wgrad_close(sub(host(layer.dw3)), sub(bwd["dw3"]), rw, fl(1), rt, "dw3")
     assert_wgrad_close(sub(host(layer.dw2)), sub(bwd["dw2"]), rw, fl(2), rt, "dw2")
     if not mism.any():
-        assert_close(host(layer.dwg), bwd["dwg"], rt, "dwg")
+        fl = router_wgrad_floor(X, fwd["route"]["probs"], fwd["route"]["topk_ids"], fwd["ye"], host(inp["dy"]),
+                                bwd["dz"], wl.inv_tau)
+        assert_close(host(layer.dwg), bwd["dwg"], rt, "dwg", floor=fl)
     # experts no token chose get an explicit zero gradient
     for e in np.nonzero(pft["tokens_per_expert"] == 0)[0]:
         assert (layer.dw1[e] == 0).all() and (layer.dw3[e] == 0).all() and (layer.dw2[e] == 0).all()

@@ -254,7 +254,8 @@ def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
     def floors(e):
         if e not in scales:
             sl = slice(o[e], o[e + 1])
-            scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl], G[sl])
+            scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl], G[sl],
+                                            host(w2[e]))
         return scales[e]
 
     rows = lambda e: o[e + 1] - o[e]
@@ -306,3 +307,25 @@ def test_rejects_bad_arguments_without_launching(xm):
     with pytest.raises(xm.XmoeError) as e:
         xm.xmoe_build_pft(ids, w, 8, pft, small_ws)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("T,d,E,k,inv_tau", [(4096, 2048, 64, 6, 1.0), (32768, 4096, 160, 8, 2.0)])
+def test_route_bwd_fullsize(xm, T, d, E, k, inv_tau):
+    """Router backward at the full sizes of the DeepSeek-MoE-16B-like and the
+    long-batch workloads (generator inputs on the GPU, oracle on the host)."""
+    orc.set_threads(min(16, orc.get_threads()))
+    g = torch.Generator(device="cuda").manual_seed(T + d)
+    x = torch.randn((T, d), generator=g, device="cuda").to(torch.bfloat16)
+    wg = (torch.randn((d, E), generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    logits = torch.randn((T, E), generator=g, device="cuda") * 2.0
+    ids, _ = workloads.random_topk(T, E, k, seed=7)
+    dtw = torch.randn((T, k), generator=g, device="cuda")
+    dx0 = torch.randn((T, d), generator=g, device="cuda").to(torch.bfloat16)
+    dx = dx0.clone()
+    dwg = torch.empty((d, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(xm.xmoe_route_bwd_workspace_size(T, d, E, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    xm.xmoe_route_bwd(x, wg, logits, ids.cuda(), dtw, dx, dwg, ws, inv_tau)
+    torch.cuda.synchronize()
+    ref = orc.route_bwd(host(logits), ids.numpy(), host(dtw), orc_in(x), orc_in(wg), inv_tau)
+    assert_close(host(dx), host(dx0) + ref["dx"], RTOL["bf16"], "dx")
+    assert_close(host(dwg), ref["dwg"], RTOL["bf16"], "dwg", floor=rss_rows(host(x), ref["dz"]))
