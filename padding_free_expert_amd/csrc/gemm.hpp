@@ -22,6 +22,8 @@
 // operands that arrive MN-contiguous are transposed in registers on the way in.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace xmoe {
@@ -113,18 +115,37 @@ __device__ __forceinline__ void seg_bounds(const GemmArgs &p, int g, int64_t *lo
     *hi = b;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
+// and each XCD has its own L2.  Tiles that share operands (the M tiles of one
+// expert reuse its weight slice; the N tiles of one row block reuse its rows)
+// are numbered consecutively, so the block -> tile map gives every XCD runs of
+// kXcdRun consecutive tiles: the tiles that run at the same time on one XCD
+// then share their operands through that XCD's L2 instead of each XCD
+// fetching them from HBM.  The map is a bijection on [0, gridDim.x).
+constexpr int kXcds = 8;
+constexpr int kXcdRun = 32;
+
+__device__ __forceinline__ int xcd_tile_order(int b, int nblocks) {
+    constexpr int W = kXcds * kXcdRun;
+    const int full = nblocks / W * W;
+    if (b >= full) return b;
+    const int xcd = b % kXcds, local = b / kXcds;
+    return (local / kXcdRun) * W + xcd * kXcdRun + local % kXcdRun;
+}
+
 // Resolve this block's tile.  Returns false when the block has no tile.
 // GM_ROWS: block -> (global m-tile, n-tile); the global m-tile is located among
 // the groups by a prefix sum of per-group tile counts computed by wave 0.
 template <int BM, int BN>
 __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
     const int tiles_n = (p.N + BN - 1) / BN;
+    const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
     if (p.group_mode == GM_KSPLIT) {
         const int tiles_m = (p.M + BM - 1) / BM;
         const int per_g = tiles_m * tiles_n;
-        const int g = blockIdx.x / per_g;
+        const int g = bid / per_g;
         if (g >= p.G) return false;
-        const int rem = blockIdx.x - g * per_g;
+        const int rem = bid - g * per_g;
         int64_t lo, hi;
         seg_bounds(p, g, &lo, &hi);
         t->g = g;
@@ -136,7 +157,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
         return true;
     }
     __shared__ int s_res[2];
-    const int mt_global = blockIdx.x / tiles_n;
+    const int mt_global = bid / tiles_n;
     const int lane = threadIdx.x;
     if (threadIdx.x == 0) s_res[0] = -1;
     __syncthreads();
@@ -178,7 +199,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
     seg_bounds(p, g, &lo, &hi);
     t->g = g;
     t->mt = s_res[1];
-    t->nt = blockIdx.x - mt_global * tiles_n;
+    t->nt = bid - mt_global * tiles_n;
     t->base = lo;
     t->Mg = static_cast<int>(hi - lo);
     t->Kg = p.K;
@@ -229,6 +250,23 @@ __device__ __forceinline__ GroupPtrs<T> group_ptrs(const GemmArgs &p, const Tile
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+// The operands' tile edges (rows past a group's end, k past K) are expressed
+// as an out-of-range offset, so loads need no branches.
+constexpr int kOob = 0x7ffffff0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint32_t n = bytes >= 0x7ffffff0 ? 0x7ffffff0u : static_cast<uint32_t>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(n), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // 8x8 transpose of 16-bit elements held as 8 rows of 16 bytes: out[j] gets
 // element j of every input row (input row i -> 16-bit lane i of out[j]).
@@ -248,33 +286,39 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
     }
 }
 
-// Global -> register staging of one operand tile of R (m or n) x BK (k) elements,
-// and register -> LDS store in the k-contiguous [R][BK+8] layout.
-template <int R, int BK, bool KC>
+// Global -> register staging of one operand tile of R (m or n) x BK (k)
+// elements, then register -> LDS in the k-contiguous [R][BK+8] layout
+// (the 16-byte row padding spreads both the 16-byte operand reads and the
+// transposed writes over all LDS banks).  Threads [TB, TB+NT) take part.
+template <int R, int BK, bool KC, int TB, int NT>
 struct TileLoader;
 
-// K-contiguous operand: element (r, k) at base[r*ld + k]
-template <int R, int BK>
-struct TileLoader<R, BK, true> {
+// K-contiguous operand: element (r, k) at byte 2*(r*ld + k) from the group base.
+template <int R, int BK, int TB, int NT>
+struct TileLoader<R, BK, true, TB, NT> {
     static constexpr int kChunks = R * BK / 8;
-    static constexpr int kIter = (kChunks + 255) / 256;
+    static constexpr int kIter = (kChunks + NT - 1) / NT;
     uint4 v[kIter];
-    __device__ __forceinline__ void load(const bf16_t *base, int64_t ld, int r0, int rmax, int k0, int kmax) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t r0, int64_t rmax, int64_t k0,
+                                         int64_t kmax) {
+        const int t = static_cast<int>(threadIdx.x) - TB;
+        if (t < 0 || t >= NT) return;
 #pragma unroll
         for (int i = 0; i < kIter; ++i) {
-            const int c = threadIdx.x + 256 * i;
+            const int c = t + NT * i;
             const int r = c / (BK / 8), kc = c % (BK / 8);
-            const int gr = r0 + r, gk = k0 + kc * 8;
-            v[i] = make_uint4(0, 0, 0, 0);
-            if ((kChunks % 256 == 0 || c < kChunks) && gr < rmax && gk < kmax)
-                v[i] = *reinterpret_cast<const uint4 *>(base + static_cast<int64_t>(gr) * ld + gk);
+            const int64_t gr = r0 + r, gk = k0 + kc * 8;
+            const bool ok = (kChunks % NT == 0 || c < kChunks) && gr < rmax && gk < kmax;
+            v[i] = buf_load16(rs, ok ? static_cast<int>((gr * ld + gk) * 2) : kOob);
         }
     }
     __device__ __forceinline__ void store(bf16_t *lds) const {
+        const int t = static_cast<int>(threadIdx.x) - TB;
+        if (t < 0 || t >= NT) return;
 #pragma unroll
         for (int i = 0; i < kIter; ++i) {
-            const int c = threadIdx.x + 256 * i;
-            if (kChunks % 256 == 0 || c < kChunks) {
+            const int c = t + NT * i;
+            if (kChunks % NT == 0 || c < kChunks) {
                 const int r = c / (BK / 8), kc = c % (BK / 8);
                 *reinterpret_cast<uint4 *>(lds + r * (BK + 8) + kc * 8) = v[i];
             }
@@ -282,47 +326,142 @@ struct TileLoader<R, BK, true> {
     }
 };
 
-// MN-contiguous operand: element (r, k) at base[k*ld + r]; moved as 8x8 blocks.
-template <int R, int BK>
-struct TileLoader<R, BK, false> {
+// MN-contiguous operand: element (r, k) at byte 2*(k*ld + r); moved as 8x8
+// blocks, k-block fastest across lanes so that the transposed LDS writes of a
+// wave land on distinct banks.
+template <int R, int BK, int TB, int NT>
+struct TileLoader<R, BK, false, TB, NT> {
     static constexpr int kBlocks = (R / 8) * (BK / 8);
-    static constexpr int kIter = (kBlocks + 255) / 256;
+    static constexpr int kIter = (kBlocks + NT - 1) / NT;
     uint4 v[kIter][8];
-    __device__ __forceinline__ void load(const bf16_t *base, int64_t ld, int r0, int rmax, int k0, int kmax) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t r0, int64_t rmax, int64_t k0,
+                                         int64_t kmax) {
+        const int t = static_cast<int>(threadIdx.x) - TB;
+        if (t < 0 || t >= NT) return;
 #pragma unroll
         for (int i = 0; i < kIter; ++i) {
-            const int b = threadIdx.x + 256 * i;
-            const int rb = b % (R / 8), kb = b / (R / 8);
-            const int gr = r0 + rb * 8;
-            const bool ok = (kBlocks % 256 == 0 || b < kBlocks) && gr < rmax;
+            const int b = t + NT * i;
+            const int kb = b % (BK / 8), rb = b / (BK / 8);
+            const int64_t gr = r0 + rb * 8;
+            const bool ok = (kBlocks % NT == 0 || b < kBlocks) && gr < rmax;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int gk = k0 + kb * 8 + q;
-                v[i][q] = make_uint4(0, 0, 0, 0);
-                if (ok && gk < kmax) v[i][q] = *reinterpret_cast<const uint4 *>(base + static_cast<int64_t>(gk) * ld + gr);
+                const int64_t gk = k0 + kb * 8 + q;
+                v[i][q] = buf_load16(rs, ok && gk < kmax ? static_cast<int>((gk * ld + gr) * 2) : kOob);
             }
         }
     }
     __device__ __forceinline__ void store(bf16_t *lds) const {
+        const int t = static_cast<int>(threadIdx.x) - TB;
+        if (t < 0 || t >= NT) return;
 #pragma unroll
         for (int i = 0; i < kIter; ++i) {
-            const int b = threadIdx.x + 256 * i;
-            if (kBlocks % 256 == 0 || b < kBlocks) {
-                const int rb = b % (R / 8), kb = b / (R / 8);
-                uint4 t[8];
-                transpose8x8(v[i], t);
+            const int b = t + NT * i;
+            if (kBlocks % NT == 0 || b < kBlocks) {
+                const int kb = b % (BK / 8), rb = b / (BK / 8);
+                uint4 o[8];
+                transpose8x8(v[i], o);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<uint4 *>(lds + (rb * 8 + j) * (BK + 8) + kb * 8) = t[j];
+                    *reinterpret_cast<uint4 *>(lds + (rb * 8 + j) * (BK + 8) + kb * 8) = o[j];
             }
         }
     }
 };
 
+// Thread ranges of the loaders: with two B matrices each takes its own half of
+// the block when its tile is small enough, so no thread does double duty.
+template <int R, int BK, bool KC>
+struct LoaderSplit {
+    static constexpr int kUnits = KC ? R * BK / 8 : (R / 8) * (BK / 8);
+};
+
+// Epilogue on 4 consecutive output columns n..n+3 of row m (all in range).
+template <int EPI, typename OutT>
+__device__ __forceinline__ void epilogue4(const GemmArgs &p, int64_t crow, int64_t coff, int m, int n,
+                                          const float (&v0)[4], const float (&v1)[4]) {
+    const int64_t row = crow + m;
+    if constexpr (EPI == EPI_ROUTER) {
+        float4 o;
+        float *po = &o.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s = __fmul_rn(v0[i], p.scale);
+            if (p.col_bias) s = __fadd_rn(s, p.col_bias[n + i]);
+            po[i] = s;
+        }
+        *reinterpret_cast<float4 *>(static_cast<float *>(p.C0) + row * p.ldc + n) = o;
+    } else if constexpr (std::is_same<OutT, float>::value) {
+        float *c = static_cast<float *>(p.C0) + coff + row * p.ldc + n;
+        if constexpr (EPI == EPI_ACCUM) {
+            float4 o = *reinterpret_cast<float4 *>(c);
+            o.x += v0[0]; o.y += v0[1]; o.z += v0[2]; o.w += v0[3];
+            *reinterpret_cast<float4 *>(c) = o;
+        } else {
+            *reinterpret_cast<float4 *>(c) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+            if (p.Cx)
+                *reinterpret_cast<float4 *>(static_cast<float *>(p.Cx) + coff + row * p.ldc + n) =
+                    make_float4(v1[0], v1[1], v1[2], v1[3]);
+        }
+    } else {
+        typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        auto pack = [](const float (&a)[4]) {
+            const f4 t = {a[0], a[1], a[2], a[3]};
+            return __builtin_convertvector(t, bf4);
+        };
+        auto unpack = [](bf4 b, float (&a)[4]) {
+            const f4 t = __builtin_convertvector(b, f4);
+            a[0] = t[0]; a[1] = t[1]; a[2] = t[2]; a[3] = t[3];
+        };
+        __bf16 *C0 = static_cast<__bf16 *>(p.C0);
+        if constexpr (EPI == EPI_STORE) {
+            *reinterpret_cast<bf4 *>(C0 + coff + row * p.ldc + n) = pack(v0);
+            if (p.Cx) *reinterpret_cast<bf4 *>(static_cast<__bf16 *>(p.Cx) + coff + row * p.ldc + n) = pack(v1);
+        } else if constexpr (EPI == EPI_ACCUM) {
+            bf4 *c = reinterpret_cast<bf4 *>(C0 + coff + row * p.ldc + n);
+            float a[4];
+            unpack(*c, a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] += v0[i];
+            *c = pack(a);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            // act = silu(H1) * H3 from the fp32 accumulators
+            float a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-v0[i]));
+                a[i] = v0[i] * sg * v1[i];
+            }
+            *reinterpret_cast<bf4 *>(C0 + row * p.ldc + n) = pack(a);
+            if (p.aux_out) {
+                __bf16 *s = static_cast<__bf16 *>(p.aux_out) + row * p.ld_aux + n;
+                *reinterpret_cast<bf4 *>(s) = pack(v0);
+                *reinterpret_cast<bf4 *>(s + p.hoff) = pack(v1);
+            }
+        } else {  // EPI_SWIGLU_BWD: v0 = dA
+            const __bf16 *s = static_cast<const __bf16 *>(p.aux) + row * p.ld_aux + n;
+            float h1[4], h3[4], g1[4], g3[4];
+            unpack(*reinterpret_cast<const bf4 *>(s), h1);
+            unpack(*reinterpret_cast<const bf4 *>(s + p.hoff), h3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[i]));
+                g1[i] = v0[i] * h3[i] * sg * (1.0f + h1[i] * (1.0f - sg));
+                g3[i] = v0[i] * h1[i] * sg;
+            }
+            *reinterpret_cast<bf4 *>(C0 + row * p.ldc + n) = pack(g1);
+            *reinterpret_cast<bf4 *>(C0 + row * p.ldc + p.hoff + n) = pack(g3);
+        }
+    }
+}
+
 // BM x BN tile per 256-thread block (4 waves as WGM x WGN), BK-deep k steps,
-// double-buffered LDS, v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
-// NB = 2 multiplies the same A tile by two B matrices (the up-projection's W1
-// and W3, or the weight gradient's dH1 and dH3).
+// double-buffered LDS, v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  The
+// B fragment is the instruction's first operand, so each lane accumulates 4
+// consecutive output columns of one output row (vector stores).  NB = 2
+// multiplies the same A tile by two B matrices (W1 and W3 of the
+// up-projection, or dH1 and dH3 of the weight gradient).
 template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int EPI, typename OutT>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
     static_assert(WGM * WGN == 4, "four waves per block");
@@ -354,20 +493,56 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
     const int nph = (p.group_mode == GM_ROWS) ? p.nphase : 1;
     const int total = ktiles * nph;
 
-    TileLoader<BM, BK, A_KC> la;
-    TileLoader<BN, BK, B_KC> lb[NB];
+    // loader thread ranges: with two B matrices whose tiles need at most half
+    // the block, each gets its own half
+    constexpr int kBUnits = LoaderSplit<BN, BK, B_KC>::kUnits;
+    constexpr bool kSplitB = NB == 2 && kBUnits <= 128;
+    constexpr int kBT0 = 0, kBN0 = kSplitB ? 128 : 256;
+    constexpr int kBT1 = kSplitB ? 128 : 0, kBN1 = kSplitB ? 128 : 256;
+    constexpr int kAUnits = LoaderSplit<BM, BK, A_KC>::kUnits;
+    constexpr int kAT = (kSplitB && kAUnits <= 128) ? 128 : 0;  // A on the half that holds B1
+    constexpr int kAN = (kSplitB && kAUnits <= 128) ? 128 : 256;
+    TileLoader<BM, BK, A_KC, kAT, kAN> la;
+    TileLoader<BN, BK, B_KC, kBT0, kBN0> lb0;
+    TileLoader<BN, BK, B_KC, kBT1, kBN1> lb1;
 
+    // Buffer resources start at the tile's origin, so every offset is small:
+    //  - a k-contiguous operand is based at its first row of the tile;
+    //  - an mn-contiguous operand of the per-group products (the expert
+    //    weights, at most K*N elements) is based at the group;
+    //  - an mn-contiguous operand whose rows are the reduction (GM_KSPLIT) is
+    //    based at the k tile.
+    const bool ksplit = p.group_mode == GM_KSPLIT;
+    auto rsrc_of = [&](const bf16_t *base, bool kc, int r0, int rows_total, int64_t ld, int k0, int64_t &rr0,
+                       int64_t &rmax, int64_t &kk0, int64_t &kmax) {
+        if (kc) {           // rows r0.., k absolute
+            rr0 = 0; rmax = rows_total - r0; kk0 = k0; kmax = t.Kg;
+            return make_rsrc(base + static_cast<int64_t>(r0) * ld, rmax * ld * 2);
+        }
+        if (ksplit) {       // k rows k0.., mn absolute
+            rr0 = r0; rmax = rows_total; kk0 = 0; kmax = t.Kg - k0;
+            return make_rsrc(base + static_cast<int64_t>(k0) * ld, kmax * ld * 2);
+        }
+        rr0 = r0; rmax = rows_total; kk0 = k0; kmax = t.Kg;   // whole [K][N] group operand
+        return make_rsrc(base, static_cast<int64_t>(t.Kg) * ld * 2);
+    };
     auto load_stage = [&](int it) {
         const int ph = it >= ktiles ? 1 : 0;
         const int k0 = (it - ph * ktiles) * BK;
-        la.load(ph ? q.A1 : q.A0, p.lda, m0, t.Mg, k0, t.Kg);
-        lb[0].load(ph ? q.B1 : q.B0, p.ldb, n0, p.N, k0, t.Kg);
-        if constexpr (NB == 2) lb[1].load(q.Bx, p.ldb, n0, p.N, k0, t.Kg);
+        int64_t r0, rmax, kk0, kmax;
+        __amdgpu_buffer_rsrc_t rs = rsrc_of(ph ? q.A1 : q.A0, A_KC, m0, t.Mg, p.lda, k0, r0, rmax, kk0, kmax);
+        la.load(rs, p.lda, r0, rmax, kk0, kmax);
+        rs = rsrc_of(ph ? q.B1 : q.B0, B_KC, n0, p.N, p.ldb, k0, r0, rmax, kk0, kmax);
+        lb0.load(rs, p.ldb, r0, rmax, kk0, kmax);
+        if constexpr (NB == 2) {
+            rs = rsrc_of(q.Bx, B_KC, n0, p.N, p.ldb, k0, r0, rmax, kk0, kmax);
+            lb1.load(rs, p.ldb, r0, rmax, kk0, kmax);
+        }
     };
     auto store_stage = [&](int buf) {
         la.store(As[buf]);
-        lb[0].store(Bs[buf][0]);
-        if constexpr (NB == 2) lb[1].store(Bs[buf][1]);
+        lb0.store(Bs[buf][0]);
+        if constexpr (NB == 2) lb1.store(Bs[buf][NB - 1]);
     };
 
     if (total > 0) {
@@ -392,7 +567,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
                     const bf16x8_t bf = *reinterpret_cast<const bf16x8_t *>(bs + j * 32 * LDK + kk);
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
-                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[b][i][j], 0, 0, 0);
+                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[b][i][j], 0, 0, 0);
                 }
             }
         }
@@ -400,19 +575,29 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
         __syncthreads();
     }
 
-    // accumulator (i, j, r): row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32 of the 32x32 block
+    // accumulator (i, j, r) of lane l holds C[row, col] with
+    //   row = i*32 + l%32,  col = j*32 + 8*(r/4) + 4*(l/32) + r%4
+    const int m_lane = m0 + wm * WTM + (lane & 31);
+    const int n_lane = n0 + wn * WTN + 4 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int m = m_lane + i * 32;
+        if (m >= t.Mg) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int n = n0 + wn * WTN + j * 32 + (lane & 31);
-                if (m < t.Mg && n < p.N)
-                    epilogue<EPI, OutT>(p, q.crow, q.coff, m, n, acc[0][i][j][r],
-                                        NB == 2 ? acc[NB - 1][i][j][r] : 0.0f);
+            for (int g = 0; g < 4; ++g) {
+                const int n = n_lane + j * 32 + 8 * g;
+                if (n >= p.N) continue;
+                float v0[4], v1[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v0[r] = acc[0][i][j][4 * g + r];
+                    v1[r] = acc[NB - 1][i][j][4 * g + r];
+                }
+                epilogue4<EPI, OutT>(p, q.crow, q.coff, m, n, v0, v1);
             }
+    }
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int EPI, typename OutT>
