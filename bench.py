@@ -22,6 +22,31 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd useful TFLOPS + tokens/s on 1 MI355X (DeepSeek-MoE shape)"
+# HBM bytes per launch of the up-projection from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# runs, recorded with a hash of the kernel sources they were taken on
+COUNTERS = os.path.join(ROOT, "profiles", "up_projection_dsmoe16b_counters.json")
+KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "ffn.hip"]
+
+
+def kernel_sources_sha1() -> str:
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "padding_free_expert_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Counter-measured bytes per launch, or None when the kernel changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha1") != kernel_sources_sha1():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
@@ -152,7 +177,7 @@ def main():
     achieved = tot_flop / (tot_ms * 1e-3) / 1e12
     roofline = {"kernel": "gemm_mfma_kernel<128,128,64,2,2,2,...,EPI_SWIGLU> (expert up-projection)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                 "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches)}
 
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
