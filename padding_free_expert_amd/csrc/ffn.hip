@@ -5,7 +5,9 @@
 // capacity -- where the article's sketch loops over the experts on the host.
 // Here one launch covers every expert: the grid is sized from the row count
 // and the expert count, and each block finds its expert and row tile from the
-// device-side offsets (see gemm.hpp).  The expert is a SwiGLU FFN (a reading:
+// device-side offsets (see gemm.hpp).  The bf16 products run on the pipelined
+// LDS-DMA kernel; tile shapes were chosen per product by timing on MI355X
+// (BM x BN x BK, NB weight matrices, S ring slots, blocks per compute unit).  The expert is a SwiGLU FFN (a reading:
 // the pages name no FFN form), so the up-projection multiplies the same rows
 // by W1 and W3 in one kernel and applies silu(H1) * H3 in its epilogue.
 //
@@ -62,7 +64,7 @@ hipError_t launch_ffn_up(int dt, const void *xs, const void *w1, const void *w3,
     p.aux_out = h13;
     p.ld_aux = 2 * static_cast<int64_t>(h);
     p.hoff = h;
-    return dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 2, true, false, EPI_SWIGLU, bf16_t>(p, s)
+    return dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, true, false, 3, EPI_SWIGLU, bf16_t, 2>(p, s)
                        : launch_gemm_f32<2, true, false, EPI_SWIGLU>(p, s);
 }
 
@@ -78,7 +80,7 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
     p.b_gstride = static_cast<int64_t>(h) * d;
     p.C0 = ye;
     p.ldc = d;
-    return dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, false, EPI_STORE, bf16_t>(p, s)
+    return dt == kBF16 ? launch_gemm_dma<256, 256, 32, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
                        : launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
 }
 
@@ -102,7 +104,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.aux = h13;
         p.ld_aux = 2 * static_cast<int64_t>(h);
         p.hoff = h;
-        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_SWIGLU_BWD, bf16_t>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<256, 128, 64, 1, true, true, 3, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
                           : launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s);
         if (err != hipSuccess) return err;
     }
@@ -120,7 +122,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.b_gstride = dh;
         p.C0 = dxs;
         p.ldc = d;
-        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_STORE, bf16_t>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<256, 256, 32, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
                           : launch_gemm_f32<1, true, true, EPI_STORE>(p, s);
         if (err != hipSuccess) return err;
     }
@@ -137,7 +139,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.Cx = dw3;
         p.ldc = h;
         p.c_gstride = dh;
-        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 2, false, false, EPI_STORE, bf16_t>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
                           : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
         if (err != hipSuccess) return err;
     }
@@ -152,7 +154,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.C0 = dw2;
         p.ldc = d;
         p.c_gstride = dh;
-        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, false, false, EPI_STORE, bf16_t>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<128, 256, 32, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
                           : launch_gemm_f32<1, false, false, EPI_STORE>(p, s);
     }
     return err;
