@@ -117,12 +117,13 @@ __device__ __forceinline__ void seg_bounds(const GemmArgs &p, int g, int64_t *lo
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
-// and each XCD has its own L2.  Tiles that share operands (the M tiles of one
-// expert reuse its weight slice; the N tiles of one row block reuse its rows)
-// are numbered consecutively, so the block -> tile map gives every XCD runs of
-// kXcdRun consecutive tiles: the tiles that run at the same time on one XCD
-// then share their operands through that XCD's L2 instead of each XCD
-// fetching them from HBM.  The map is a bijection on [0, gridDim.x).
+// and each XCD has its own L2.  Tiles that share operands are numbered
+// consecutively (a group's tiles together; within a GM_ROWS group the m-tiles
+// of one n-tile, which read the same weight slice at the same k, are adjacent),
+// and the block -> tile map gives every XCD runs of kXcdRun consecutive tiles:
+// the tiles that run at the same time on one XCD then share their operands
+// through that XCD's L2 instead of each XCD fetching them from HBM.  The map
+// is a bijection on [0, nblocks).
 constexpr int kXcds = 8;
 constexpr int kXcdRun = 32;
 
@@ -135,15 +136,15 @@ __device__ __forceinline__ int xcd_tile_order(int b, int nblocks) {
 }
 
 // Resolve this block's tile.  Returns false when the block has no tile.
-// GM_ROWS: block -> (global m-tile, n-tile); the global m-tile is located among
-// the groups by a prefix sum of per-group tile counts computed by wave 0.
+// GM_ROWS: the group is located by a prefix sum of per-group m-tile counts
+// computed by wave 0 (group g owns tiles [exc*tiles_n, inc*tiles_n)).
 template <int BM, int BN>
 __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
     const int tiles_n = (p.N + BN - 1) / BN;
-    const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
     if (p.group_mode == GM_KSPLIT) {
         const int tiles_m = (p.M + BM - 1) / BM;
         const int per_g = tiles_m * tiles_n;
+        const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
         const int g = bid / per_g;
         if (g >= p.G) return false;
         const int rem = bid - g * per_g;
@@ -157,8 +158,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
         t->Kg = static_cast<int>(hi - lo);
         return true;
     }
-    __shared__ int s_res[2];
-    const int mt_global = bid / tiles_n;
+    __shared__ int s_res[3];
     const int lane = threadIdx.x;
     if (threadIdx.x == 0) s_res[0] = -1;
     __syncthreads();
@@ -178,6 +178,8 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
             if (lane >= off) inc += v;
         }
         const int exc = inc - cnt;
+        const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
+        const int mt_global = bid / tiles_n;   // past the last group's tiles: no tile
         if (mt_global >= exc && mt_global < inc) {
             int b = exc;
             for (int g = g0; g < g1; ++g) {
@@ -185,8 +187,11 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
                 seg_bounds(p, g, &lo, &hi);
                 const int n = static_cast<int>((hi - lo + BM - 1) / BM);
                 if (mt_global < b + n) {
+                    // the group's tiles are bid in [b*tiles_n, (b+n)*tiles_n), m-tile fastest
+                    const int local = bid - b * tiles_n;
                     s_res[0] = g;
-                    s_res[1] = mt_global - b;
+                    s_res[1] = local % n;
+                    s_res[2] = local / n;
                     break;
                 }
                 b += n;
@@ -200,7 +205,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
     seg_bounds(p, g, &lo, &hi);
     t->g = g;
     t->mt = s_res[1];
-    t->nt = bid - mt_global * tiles_n;
+    t->nt = s_res[2];
     t->base = lo;
     t->Mg = static_cast<int>(hi - lo);
     t->Kg = p.K;
