@@ -80,7 +80,7 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
     p.b_gstride = static_cast<int64_t>(h) * d;
     p.C0 = ye;
     p.ldc = d;
-    return dt == kBF16 ? launch_gemm_dma<256, 256, 32, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+    return dt == kBF16 ? launch_gemm_dma<128, 256, 32, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s)
                        : launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
 }
 
@@ -104,7 +104,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.aux = h13;
         p.ld_aux = 2 * static_cast<int64_t>(h);
         p.hoff = h;
-        err = dt == kBF16 ? launch_gemm_dma<256, 128, 64, 1, true, true, 3, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<128, 128, 64, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s)
                           : launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s);
         if (err != hipSuccess) return err;
     }

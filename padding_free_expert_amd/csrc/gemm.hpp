@@ -910,6 +910,137 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     //   row = i*32 + l%32,  col = j*32 + 8*(r/4) + 4*(l/32) + r%4
     const int m_lane = m0 + wm * WTM + (lane & 31);
     const int n_lane = n0 + wn * WTN + 4 * (lane >> 5);
+    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
+        // Staged epilogue: each output matrix goes through the (now idle) ring
+        // as a padded row-major bf16 tile, then leaves in 16-byte row chunks
+        // (16 lanes per 256-byte row segment) instead of 8-byte pieces.
+        constexpr int LDC = BN + 8;
+        // two passes (one per row half, i.e. per wave row) when the tile does not fit the ring
+        constexpr int kPass = BM * LDC * 2 <= S * kStage ? 1 : 2;
+        constexpr int RP = BM / kPass;  // rows per pass
+        static_assert(RP * LDC * 2 <= S * kStage, "output tile must fit the ring");
+        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        __bf16 *cs = reinterpret_cast<__bf16 *>(smem);
+        const int nout = EPI == EPI_SWIGLU ? (p.aux_out ? 3 : 1) : ((NB == 2 && p.Cx) ? 2 : 1);
+        __syncthreads();  // every wave is done with the ring
+        for (int o = 0; o < nout; ++o) {
+            __bf16 *dst;
+            int64_t ld;
+            if constexpr (EPI == EPI_SWIGLU) {
+                dst = o == 0 ? static_cast<__bf16 *>(p.C0) + q.crow * p.ldc
+                             : static_cast<__bf16 *>(p.aux_out) + q.crow * p.ld_aux + (o == 2 ? p.hoff : 0);
+                ld = o == 0 ? p.ldc : p.ld_aux;
+            } else {
+                dst = static_cast<__bf16 *>(o == 0 ? p.C0 : p.Cx) + q.coff + q.crow * p.ldc;
+                ld = p.ldc;
+            }
+            for (int pass = 0; pass < kPass; ++pass) {
+                if (kPass == 1 || wm == pass) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                f4_t v;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float a = acc[0][i][j][4 * g + r], b = acc[NB - 1][i][j][4 * g + r];
+                                    float x;
+                                    if constexpr (EPI == EPI_SWIGLU)
+                                        x = o == 0 ? a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * b : (o == 1 ? a : b);
+                                    else
+                                        x = o == 0 ? a : b;
+                                    v[r] = x;
+                                }
+                                const int row = (kPass == 1 ? wm * WTM : 0) + i * 32 + (lane & 31);
+                                const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                                *reinterpret_cast<bf4_t *>(cs + row * LDC + col) = __builtin_convertvector(v, bf4_t);
+                            }
+                }
+                __syncthreads();
+#pragma unroll 4
+                for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+                    const int row = c / (BN / 8), c8 = c % (BN / 8);
+                    const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
+                    if (m < t.Mg && n < p.N)
+                        *reinterpret_cast<uint4 *>(dst + m * ld + n) =
+                            *reinterpret_cast<const uint4 *>(cs + row * LDC + 8 * c8);
+                }
+                if (o + 1 < nout || pass + 1 < kPass) __syncthreads();
+            }
+        }
+        return;
+    }
+    if constexpr (std::is_same<OutT, bf16_t>::value && EPI == EPI_SWIGLU_BWD) {
+        // Staged SwiGLU backward: the saved H1 and H3 tiles come into the ring
+        // with 16-byte row reads, each lane turns its dA values and the H1/H3 at
+        // the same places into dH1/dH3 in place, and both tiles leave in
+        // 16-byte row chunks.
+        constexpr int LDC = BN + 8;
+        constexpr int kPass = 2 * BM * LDC * 2 <= S * kStage ? 1 : 2;
+        constexpr int RP = BM / kPass;
+        static_assert(2 * RP * LDC * 2 <= S * kStage, "H1/H3 tiles must fit the ring");
+        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        __bf16 *c1 = reinterpret_cast<__bf16 *>(smem), *c3 = c1 + RP * LDC;
+        const __bf16 *aux = static_cast<const __bf16 *>(p.aux) + q.crow * p.ld_aux;
+        __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.crow * p.ldc;
+        __syncthreads();  // every wave is done with the ring
+        for (int pass = 0; pass < kPass; ++pass) {
+#pragma unroll 4
+            for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+                const int row = c / (BN / 8), c8 = c % (BN / 8);
+                const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
+                if (m < t.Mg && n < p.N) {
+                    *reinterpret_cast<uint4 *>(c1 + row * LDC + 8 * c8) =
+                        *reinterpret_cast<const uint4 *>(aux + m * p.ld_aux + n);
+                    *reinterpret_cast<uint4 *>(c3 + row * LDC + 8 * c8) =
+                        *reinterpret_cast<const uint4 *>(aux + m * p.ld_aux + p.hoff + n);
+                }
+            }
+            __syncthreads();
+            if (kPass == 1 || wm == pass) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int row = (kPass == 1 ? wm * WTM : 0) + i * 32 + (lane & 31);
+                            const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                            bf4_t *p1 = reinterpret_cast<bf4_t *>(c1 + row * LDC + col);
+                            bf4_t *p3 = reinterpret_cast<bf4_t *>(c3 + row * LDC + col);
+                            const f4_t h1 = __builtin_convertvector(*p1, f4_t), h3 = __builtin_convertvector(*p3, f4_t);
+                            f4_t g1, g3;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float v0 = acc[0][i][j][4 * g + r];
+                                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
+                                g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
+                                g3[r] = v0 * h1[r] * sg;
+                            }
+                            *p1 = __builtin_convertvector(g1, bf4_t);
+                            *p3 = __builtin_convertvector(g3, bf4_t);
+                        }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+                const int row = c / (BN / 8), c8 = c % (BN / 8);
+                const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
+                if (m < t.Mg && n < p.N) {
+                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) =
+                        *reinterpret_cast<const uint4 *>(c1 + row * LDC + 8 * c8);
+                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
+                        *reinterpret_cast<const uint4 *>(c3 + row * LDC + 8 * c8);
+                }
+            }
+            if (pass + 1 < kPass) __syncthreads();
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m_lane + i * 32;
