@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsmoe16b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lean", action="store_true",
+                    help="recompute H1/H3 in the backward instead of keeping them from the forward")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: pick for ~10-30 s)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,7 +104,7 @@ def main():
     inp = workloads.generate(wl, device="cuda", backward=True)
     weights = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias")
                if k in inp}
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True)
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=args.lean)
     x, dy = inp["x"], inp["dy"]
     stream = torch.cuda.current_stream()
 
@@ -151,23 +153,26 @@ def main():
             prev = e
 
     # roofline of the dominant kernel: the up-projection (W1|W3 + SwiGLU), launched
-    # once for the routed experts and once for the shared experts per step
+    # once for the routed experts (rows gathered from x through the PFT's
+    # token_ids) and once for the shared experts per step
     R, d, h = wl.R, wl.d, wl.h
-    up_launches = [(layer.xs, weights["w1"], weights["w3"], layer.pft.expert_offsets, layer.act, layer.h13,
+    up_launches = [(lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, weights["w1"], weights["w3"],
+                                                        layer.pft.expert_offsets, layer.act, layer.h13),
                     4.0 * R * d * h)]
     if layer.shared:
         hs = layer.hs
-        up_launches.append((x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0), layer.sh_off,
-                            layer.sh_act, layer.sh_h13, 4.0 * wl.T * d * hs))
+        up_launches.append((lambda: xm.xmoe_expert_ffn_up(x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0),
+                                                          layer.sh_off, layer.sh_act, layer.sh_h13),
+                            4.0 * wl.T * d * hs))
     n_rep = 20
     tot_ms, tot_flop, per = 0.0, 0.0, []
-    for (a, w1, w3, off, act, h13, fl) in up_launches:
+    for (launch, fl) in up_launches:
         for _ in range(3):
-            xm.xmoe_expert_ffn_up(a, w1, w3, off, act, h13)
+            launch()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n_rep):
-            xm.xmoe_expert_ffn_up(a, w1, w3, off, act, h13)
+            launch()
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / n_rep
@@ -184,10 +189,12 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "h": wl.h, "k": wl.k,
-                      "n_shared": wl.n_shared, "h_shared": wl.h_shared, "passes": "fwd+bwd"},
+                      "n_shared": wl.n_shared, "h_shared": wl.h_shared, "passes": "fwd+bwd",
+                      "h13": "recomputed" if args.lean else "saved"},
            "tokens_per_s": round(tok_s, 1), "gpu_ms_per_step": round(gpu_ms, 4),
            "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
            "useful_gflop_per_step": round(flops["total"] / 1e9, 2),
+           "saved_activation_mb": round(layer.saved_bytes() / 1e6, 1),
            "breakdown_ms": {k: round(v, 4) for k, v in breakdown.items()},
            "roofline": roofline}
 
@@ -211,7 +218,7 @@ def cpu_baseline(wl, inp, sample_tokens):
     def bits(t):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    n = sample_tokens or 256
+    n = sample_tokens or 512
     o = {k: bits(v) for k, v in inp.items() if v is not None and k not in ("logit_bias", "select_bias")}
     for k in ("logit_bias", "select_bias"):
         if inp.get(k) is not None:

@@ -177,6 +177,32 @@ xmoe_status xmoe_expert_ffn_down(const void *act, const void *w2, xmoe_dtype dty
                                  int32_t h, void *ye, void *stream);
 
 /*
+ * Up-projection with the dispatch gather fused into the operand loads (X-MoE
+ * article, section 2.1.2: the PFT's token_ids name each row's source token):
+ * the same products as xmoe_expert_ffn_up with xs[r] replaced by
+ * x[token_ids[r]], so the expert-sorted copy xs is never materialised.
+ * x [T,d]; token_ids: DEVICE int32 [rows] with values in [0, T) (the PFT's
+ * token_ids satisfy this; bf16 reads outside x return 0, fp32 reads are not
+ * checked).  Results are bitwise those of xmoe_dispatch + xmoe_expert_ffn_up.
+ * Limits as xmoe_expert_ffn_up, plus T * d * element size < 2^31 bytes.
+ */
+xmoe_status xmoe_expert_ffn_up_gather(const void *x, const int32_t *token_ids, const void *w1,
+                                      const void *w3, xmoe_dtype dtype,
+                                      const int32_t *expert_offsets, int32_t E, int64_t T,
+                                      int64_t rows, int32_t d, int32_t h, void *act, void *h13,
+                                      void *stream);
+
+/*
+ * Whole expert FFN with the gather fused: xmoe_expert_ffn_up_gather followed
+ * by xmoe_expert_ffn_down.  Same arguments and limits as those two calls.
+ */
+xmoe_status xmoe_expert_ffn_gather(const void *x, const int32_t *token_ids, const void *w1,
+                                   const void *w3, const void *w2, xmoe_dtype dtype,
+                                   const int32_t *expert_offsets, int32_t E, int64_t T,
+                                   int64_t rows, int32_t d, int32_t h, void *act, void *h13,
+                                   void *ye, void *stream);
+
+/*
  * Whole expert FFN: xmoe_expert_ffn_up followed by xmoe_expert_ffn_down.
  * act [rows,h] is required (it is the down-projection's input and the
  * backward's); h13 may be NULL for a forward-only pass.

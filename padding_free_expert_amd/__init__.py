@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "XmoeError", "PFT", "lib_path", "xmoe_version", "xmoe_query_device", "xmoe_route",
     "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn_up",
-    "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_combine", "xmoe_combine_bwd",
+    "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
+    "xmoe_combine", "xmoe_combine_bwd",
     "xmoe_expert_ffn_bwd", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
 ]
 
@@ -60,6 +61,10 @@ _lib_up = _sig("xmoe_expert_ffn_up", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i
 _lib_down = _sig("xmoe_expert_ffn_down", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
 _lib_ffn = _sig("xmoe_expert_ffn", [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp,
                                     _vp, _vp])
+_lib_up_g = _sig("xmoe_expert_ffn_up_gather", [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32,
+                                                _vp, _vp, _vp])
+_lib_ffn_g = _sig("xmoe_expert_ffn_gather", [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32,
+                                             _i32, _vp, _vp, _vp, _vp])
 _lib_combine = _sig("xmoe_combine", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp])
 _lib_combine_bwd = _sig("xmoe_combine_bwd", [_vp, _vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int,
                                              _vp, _vp, _vp])
@@ -178,6 +183,22 @@ def xmoe_expert_ffn_up(xs, w1, w3, expert_offsets, act, h13=None, stream=None):
     E, _, h = w1.shape
     _check(_lib_up(_ptr(xs), _ptr(w1), _ptr(w3), _dt(xs), _ptr(expert_offsets), E, rows, d, h, _ptr(act),
                    _ptr(h13), _stream(stream)), "xmoe_expert_ffn_up")
+
+
+def xmoe_expert_ffn_up_gather(x, token_ids, w1, w3, expert_offsets, act, h13=None, stream=None):
+    T, d = x.shape
+    E, _, h = w1.shape
+    rows = token_ids.shape[0]
+    _check(_lib_up_g(_ptr(x), _ptr(token_ids), _ptr(w1), _ptr(w3), _dt(x), _ptr(expert_offsets), E, T, rows, d, h,
+                     _ptr(act), _ptr(h13), _stream(stream)), "xmoe_expert_ffn_up_gather")
+
+
+def xmoe_expert_ffn_gather(x, token_ids, w1, w3, w2, expert_offsets, act, ye, h13=None, stream=None):
+    T, d = x.shape
+    E, _, h = w1.shape
+    rows = token_ids.shape[0]
+    _check(_lib_ffn_g(_ptr(x), _ptr(token_ids), _ptr(w1), _ptr(w3), _ptr(w2), _dt(x), _ptr(expert_offsets), E, T,
+                      rows, d, h, _ptr(act), _ptr(h13), _ptr(ye), _stream(stream)), "xmoe_expert_ffn_gather")
 
 
 def xmoe_expert_ffn_down(act, w2, expert_offsets, ye, stream=None):

@@ -118,6 +118,16 @@ xmoe::PftPtrs to_ptrs(const xmoe_pft *p) {
     return {p->token_ids, p->expert_ids, p->tokens_per_expert, p->expert_offsets, p->combine_weights, p->slot_to_row};
 }
 
+// x is read through the row map with 32-bit buffer offsets
+xmoe_status check_gather(const void *x, const int32_t *token_ids, int64_t T, int64_t rows, int32_t d,
+                         xmoe_dtype dtype) {
+    REQUIRE(rows == 0 || (x && token_ids), XMOE_ERR_INVALID_VALUE, "x and token_ids are required");
+    REQUIRE(T >= 1, XMOE_ERR_INVALID_VALUE, "T must be >= 1");
+    REQUIRE(T * static_cast<int64_t>(d) * (dtype == XMOE_BF16 ? 2 : 4) < (int64_t{1} << 31), XMOE_ERR_UNSUPPORTED,
+            "x must be smaller than 2^31 bytes to be gathered");
+    REQUIRE(aligned16(x), XMOE_ERR_UNSUPPORTED, "x must be 16-byte aligned");
+    return XMOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -198,7 +208,8 @@ xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, x
     REQUIRE(aligned16(xs) && aligned16(w1) && aligned16(w3) && aligned16(act) && aligned16(h13),
             XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_up(dtype, xs, w1, w3, expert_offsets, E, rows, d, h, act, h13, S(stream)),
+    return hip_status(xmoe::launch_ffn_up(dtype, xs, nullptr, 0, w1, w3, expert_offsets, E, rows, d, h, act, h13,
+                                          S(stream)),
                       "xmoe_expert_ffn_up launch");
 }
 
@@ -213,6 +224,40 @@ xmoe_status xmoe_expert_ffn_down(const void *act, const void *w2, xmoe_dtype dty
                       "xmoe_expert_ffn_down launch");
 }
 
+
+xmoe_status xmoe_expert_ffn_up_gather(const void *x, const int32_t *token_ids, const void *w1, const void *w3,
+                                      xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E, int64_t T,
+                                      int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(w1 && w3 && (rows == 0 || act), XMOE_ERR_INVALID_VALUE, "w1, w3 and act are required");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    TRY(check_gather(x, token_ids, T, rows, d, dtype));
+    REQUIRE(aligned16(w1) && aligned16(w3) && aligned16(act) && aligned16(h13), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_up(dtype, x, token_ids, T, w1, w3, expert_offsets, E, rows, d, h, act, h13,
+                                          S(stream)),
+                      "xmoe_expert_ffn_up_gather launch");
+}
+
+xmoe_status xmoe_expert_ffn_gather(const void *x, const int32_t *token_ids, const void *w1, const void *w3,
+                                   const void *w2, xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                                   int64_t T, int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *ye,
+                                   void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(w1 && w3 && w2 && (rows == 0 || (act && ye)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    TRY(check_gather(x, token_ids, T, rows, d, dtype));
+    REQUIRE(aligned16(w1) && aligned16(w3) && aligned16(w2) && aligned16(act) && aligned16(h13) && aligned16(ye),
+            XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    hipError_t e = xmoe::launch_ffn_up(dtype, x, token_ids, T, w1, w3, expert_offsets, E, rows, d, h, act, h13,
+                                       S(stream));
+    if (e != hipSuccess) return hip_status(e, "xmoe_expert_ffn_gather up-projection launch");
+    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, S(stream)),
+                      "xmoe_expert_ffn_gather down-projection launch");
+}
+
 xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, const void *w2, xmoe_dtype dtype,
                             const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h, void *act,
                             void *h13, void *ye, void *stream) {
@@ -224,7 +269,7 @@ xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, cons
                 aligned16(ye),
             XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    hipError_t e = xmoe::launch_ffn_up(dtype, xs, w1, w3, expert_offsets, E, rows, d, h, act, h13, S(stream));
+    hipError_t e = xmoe::launch_ffn_up(dtype, xs, nullptr, 0, w1, w3, expert_offsets, E, rows, d, h, act, h13, S(stream));
     if (e != hipSuccess) return hip_status(e, "xmoe_expert_ffn up-projection launch");
     return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, S(stream)),
                       "xmoe_expert_ffn down-projection launch");

@@ -12,7 +12,8 @@
 // by W1 and W3 in one kernel and applies silu(H1) * H3 in its epilogue.
 //
 // Products (rows of expert e = [off[e], off[e+1]); weights row-major):
-//   up       act = silu(xs.W1) * (xs.W3)        A = xs, B = W1 | W3 (n-contiguous)
+//   up       act = silu(xs.W1) * (xs.W3)        A = xs, B = W1 | W3 (n-contiguous);
+//                                               or A row r = x[token_ids[r]] (gather fused)
 //   down     ye  = act.W2                       A = act, B = W2 (n-contiguous)
 //   dgrad2   dA  = dye.W2^T -> dH1, dH3         A = dye, B = W2 read k-contiguous
 //   dgrad1   dxs = dH1.W1^T + dH3.W3^T          two k phases, B read k-contiguous
@@ -48,9 +49,12 @@ GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
 
 }  // namespace
 
-hipError_t launch_ffn_up(int dt, const void *xs, const void *w1, const void *w3, const int32_t *offsets, int E,
-                         int64_t rows, int d, int h, void *act, void *h13, hipStream_t s) {
+hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *w1,
+                         const void *w3, const int32_t *offsets, int E, int64_t rows, int d, int h, void *act,
+                         void *h13, hipStream_t s) {
     GemmArgs p = rows_args(offsets, E, rows);
+    p.a_map = row_map;  // the gather fused into the A loads: row r reads xs[row_map[r]]
+    p.a_map_rows = map_rows;
     p.N = h;
     p.K = d;
     p.A0 = xs;

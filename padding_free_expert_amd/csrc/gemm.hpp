@@ -51,6 +51,11 @@ struct GemmArgs {
     int hoff;                // column offset of the H3 half in [H1|H3]
     float scale;             // EPI_ROUTER
     const float *col_bias;   // EPI_ROUTER (optional)
+    // GM_ROWS with a k-contiguous A (bf16 pipelined and fp32 kernels only):
+    // when a_map is set, row r of the rows-space reads A0 row a_map[r] (A0 has
+    // a_map_rows rows), i.e. the dispatch gather happens in the operand loads.
+    const int32_t *a_map;
+    int64_t a_map_rows;
 };
 
 // ---------------------------------------------------------------- epilogues
@@ -705,10 +710,25 @@ struct DmaPlan {
             }
         }
     }
-    // instruction i of k block k0 (KC: kadd = 2*k0; MN: the buffer starts at row k0)
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, bool live, int k0, int kadd, uint32_t dst,
-                                          int wave, int i) const {
-        lds_dma16(rs, live && k0 < lim[i] ? base[i] + kadd : kOob, dst + (i * 4 + wave) * 1024);
+    // KC rows read through a row map: tile row `row` < rmax is memory row rmap[row]
+    __device__ __forceinline__ void init_mapped(int wave, int lane, int64_t ld, const int32_t *rmap, int rmax,
+                                                int kmax) {
+        static_assert(KC, "row maps apply to k-contiguous operands");
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+            const int o = (i * 4 + wave) * 1024 + lane * 16;
+            const int row = o / kRowBytes, s = (o % kRowBytes) / 16;
+            const int c = s ^ swz_kc(row, kCpr);
+            const int64_t mr = row < rmax ? rmap[row] : 0;
+            base[i] = static_cast<int>((mr * ld + 8 * c) * 2);
+            lim[i] = row < rmax ? kmax - 8 * c : INT_MIN;
+        }
+    }
+    // instruction i of the k block starting at kc (INT_MAX: a block past the end);
+    // KC: kadd = 2*k0; MN: the buffer starts at the block's first k row
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kc, int kadd, uint32_t dst, int wave,
+                                          int i) const {
+        lds_dma16(rs, kc < lim[i] ? base[i] + kadd : kOob, dst + (i * 4 + wave) * 1024);
     }
 };
 
@@ -778,8 +798,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
     PA pa;
     PB pb;
-    if constexpr (A_KC) pa.init(wave, lane, p.lda, 0, t.Mg - m0, t.Kg);
-    else pa.init(wave, lane, p.lda, m0, t.Mg, t.Kg);
+    const bool amap = A_KC && p.a_map != nullptr && p.group_mode == GM_ROWS;
+    if constexpr (A_KC) {
+        if (amap) pa.init_mapped(wave, lane, p.lda, p.a_map + t.base + m0, t.Mg - m0, t.Kg);
+        else pa.init(wave, lane, p.lda, 0, t.Mg - m0, t.Kg);
+    } else {
+        pa.init(wave, lane, p.lda, m0, t.Mg, t.Kg);
+    }
     if constexpr (B_KC) pb.init(wave, lane, p.ldb, 0, p.N - n0, t.Kg);
     else pb.init(wave, lane, p.ldb, n0, p.N, t.Kg);
 
@@ -794,7 +819,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const __amdgpu_buffer_rsrc_t none = make_rsrc(q.A0, 0);  // placeholder for mn-contiguous operands
     __amdgpu_buffer_rsrc_t ra0 = none, ra1 = none, rb0 = none, rb1 = none, rbx = none;
     if constexpr (A_KC) {
-        ra0 = rs_kc(q.A0, m0, t.Mg, p.lda);
+        // with a row map the buffer spans the whole gathered matrix (its
+        // a_map_rows * lda elements must stay below 2^31 bytes)
+        ra0 = amap ? make_rsrc(p.A0, p.a_map_rows * p.lda * 2) : rs_kc(q.A0, m0, t.Mg, p.lda);
         ra1 = q.A1 ? rs_kc(q.A1, m0, t.Mg, p.lda) : ra0;
     }
     if constexpr (B_KC) {
@@ -803,22 +830,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         rbx = q.Bx ? rs_kc(q.Bx, n0, p.N, p.ldb) : rb0;
     }
 
-    // Load instruction `part` (0 .. kL-1) of k block `st` into the slot at `dst`.
-    // Blocks past the end issue out-of-range loads that write zeros to a slot
-    // nobody reads, which keeps the count of loads in flight uniform.
-    auto issue_part = [&](int st, uint32_t dst, int part) {
+    // Everything a k block's loads need, computed once per block: the buffers
+    // (an mn-contiguous operand's buffer starts at the block's first k row),
+    // the k offset of k-contiguous operands, and kc = k0, or INT_MAX for blocks
+    // past the end, which makes every load of such a block out of range (it
+    // writes zeros to a slot nobody reads and keeps the count of loads in
+    // flight uniform).
+    struct StagePlan {
+        __amdgpu_buffer_rsrc_t ra, rb, rx;
+        int kc, kadd;
+    };
+    auto plan_stage = [&](int st) {
+        StagePlan sp;
         const bool live = st < total;
         const int ph = (live && st >= ktiles) ? 1 : 0;
         const int k0 = live ? (st - ph * ktiles) * BK : 0;
+        sp.kc = live ? k0 : INT_MAX;
+        sp.kadd = 2 * k0;
+        if constexpr (A_KC) sp.ra = ph ? ra1 : ra0;
+        else sp.ra = rs_mn(ph ? q.A1 : q.A0, p.lda, k0);
+        if constexpr (B_KC) {
+            sp.rb = ph ? rb1 : rb0;
+            sp.rx = rbx;
+        } else {
+            sp.rb = rs_mn(ph ? q.B1 : q.B0, p.ldb, k0);
+            sp.rx = NB == 2 ? rs_mn(q.Bx, p.ldb, k0) : sp.rb;
+        }
+        return sp;
+    };
+    // load instruction `part` (0 .. kL-1) of a k block into the slot at `dst`
+    auto issue_part = [&](const StagePlan &sp, uint32_t dst, int part) {
         if (part < PA::kN) {
-            if constexpr (A_KC) pa.issue(ph ? ra1 : ra0, live, k0, 2 * k0, dst, wave, part);
-            else pa.issue(rs_mn(ph ? q.A1 : q.A0, p.lda, k0), live, k0, 0, dst, wave, part);
+            pa.issue(sp.ra, sp.kc, A_KC ? sp.kadd : 0, dst, wave, part);
         } else {
             const int pp = part - PA::kN;
             const int b = pp / PB::kN, i = pp % PB::kN;
-            const uint32_t d = dst + kABytes + b * kBBytes;
-            if constexpr (B_KC) pb.issue(b ? rbx : (ph ? rb1 : rb0), live, k0, 2 * k0, d, wave, i);
-            else pb.issue(rs_mn(b ? q.Bx : (ph ? q.B1 : q.B0), p.ldb, k0), live, k0, 0, d, wave, i);
+            pb.issue(b ? sp.rx : sp.rb, sp.kc, B_KC ? sp.kadd : 0, dst + kABytes + b * kBBytes, wave, i);
         }
     };
 
@@ -860,9 +907,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 
     // prologue: blocks 0 .. S-2 in flight; wait for block 0; its first fragments
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
+    for (int s = 0; s < S - 1; ++s) {
+        const StagePlan sp = plan_stage(s);
 #pragma unroll
-        for (int u = 0; u < kL; ++u) issue_part(s, sbase + s * kStage, u);
+        for (int u = 0; u < kL; ++u) issue_part(sp, sbase + s * kStage, u);
+    }
     wait_vmem<kL * (S - 2)>();
     __syncthreads();
 #pragma unroll
@@ -873,6 +922,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         const uint32_t sa = sbase + cur * kStage;
         const int nxt = cur + 1 == S ? 0 : cur + 1;
         const uint32_t sf = sbase + (cur == 0 ? S - 1 : cur - 1) * kStage;  // freed by the last barrier
+        const StagePlan sp = plan_stage(it + S - 1);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const int c = kk & 1, n = c ^ 1;
@@ -897,9 +947,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
                     for (int z = 0; z < DPQ; ++z) {
                         const int part = kk * DPK + qq * DPQ + z;
-                        if (qq * DPQ + z < DPK && part < kL) issue_part(it + S - 1, sf, part);
+                        if (qq * DPQ + z < DPK && part < kL) issue_part(sp, sf, part);
                     }
                 }
+#ifdef XMOE_GEMM_PIN_ORDER
+                __builtin_amdgcn_sched_barrier(0);
+#endif
             }
         }
         cur = nxt;
@@ -1106,7 +1159,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
                 const int gm = m0 + mm, gk = k0 + kk;
                 float va = 0.0f;
                 if (gm < t.Mg && gk < t.Kg)
-                    va = A_KC ? A[static_cast<int64_t>(gm) * p.lda + gk] : A[static_cast<int64_t>(gk) * p.lda + gm];
+                    if (A_KC && p.a_map && p.group_mode == GM_ROWS)
+                        va = static_cast<const float *>(p.A0)[static_cast<int64_t>(p.a_map[t.base + gm]) * p.lda + gk];
+                    else
+                        va = A_KC ? A[static_cast<int64_t>(gm) * p.lda + gk] : A[static_cast<int64_t>(gk) * p.lda + gm];
                 As[kk][mm] = va;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {

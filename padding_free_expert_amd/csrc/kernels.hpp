@@ -41,8 +41,10 @@ hipError_t launch_combine_bwd(int dt, const void *dy, const void *ye, const int3
                               hipStream_t s);
 
 // expert FFN
-hipError_t launch_ffn_up(int dt, const void *xs, const void *w1, const void *w3, const int32_t *offsets, int E,
-                         int64_t rows, int d, int h, void *act, void *h13, hipStream_t s);
+// row_map: NULL (rows of xs) or the PFT token_ids (rows of x, which has map_rows rows)
+hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *w1,
+                         const void *w3, const int32_t *offsets, int E, int64_t rows, int d, int h, void *act,
+                         void *h13, hipStream_t s);
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows,
                            int d, int h, void *ye, hipStream_t s);
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,

@@ -13,8 +13,9 @@ from typing import Dict, Optional
 import torch
 
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_workspace_size, xmoe_combine, xmoe_combine_bwd,
-               xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_route,
-               xmoe_route_bwd, xmoe_route_bwd_workspace_size)
+               xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_expert_ffn_gather,
+               xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
+               xmoe_route_bwd_workspace_size)
 
 
 class PaddingFreeMoE:
@@ -22,10 +23,17 @@ class PaddingFreeMoE:
 
     weights: dict with wg [d,E], w1/w3 [E,d,h], w2 [E,h,d]; optional shared-expert
     weights s1/s3 [d, n*h_s], s2 [n*h_s, d] (the shared experts side by side),
-    logit_bias / select_bias fp32 [E]."""
+    logit_bias / select_bias fp32 [E].
+
+    The forward never materialises the expert-sorted copy of x: the gather is
+    fused into the up-projection's operand loads (X-MoE article, section 2.1.2).
+    The backward re-gathers it once, as scratch, for the weight gradient of
+    W1/W3.  lean=True also drops the saved pre-activations H1/H3 and recomputes
+    them in the backward (the same kernel, so bitwise the same values): what
+    the backward needs from the forward shrinks to act, ye and the routing."""
 
     def __init__(self, weights: Dict[str, torch.Tensor], T: int, k: int, inv_tau: float = 1.0,
-                 backward: bool = True):
+                 backward: bool = True, lean: bool = False):
         self.w = weights
         wg, w1 = weights["wg"], weights["w1"]
         self.dtype = wg.dtype
@@ -35,6 +43,7 @@ class PaddingFreeMoE:
         self.h = w1.shape[2]
         self.shared = weights.get("s1") is not None
         self.backward_enabled = backward
+        self.lean = lean
         dev, dt = self.device, self.dtype
         T, d, E, h, R = T, self.d, self.E, self.h, T * k
         f32 = dict(dtype=torch.float32, device=dev)
@@ -43,7 +52,8 @@ class PaddingFreeMoE:
         self.logits = torch.empty((T, E), **f32)
         self.pft = PFT(T, E, k, dev)
         self.pft_ws = torch.empty(max(xmoe_build_pft_workspace_size(T, E, k), 16), dtype=torch.uint8, device=dev)
-        self.xs = torch.empty((R, d), dtype=dt, device=dev)
+        # scratch of the backward (re-gathered rows), not kept from the forward
+        self.xs = torch.empty((R, d), dtype=dt, device=dev) if backward else None
         self.act = torch.empty((R, h), dtype=dt, device=dev)
         self.h13 = torch.empty((R, 2 * h), dtype=dt, device=dev) if backward else None
         self.ye = torch.empty((R, d), dtype=dt, device=dev)
@@ -89,15 +99,15 @@ class PaddingFreeMoE:
         mark("route")
         xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=stream)
         mark("build_pft")
-        xmoe_dispatch(x, self.k, self.pft, self.xs, stream=stream)
-        mark("dispatch")
-        xmoe_expert_ffn(self.xs, w["w1"], w["w3"], w["w2"], self.pft.expert_offsets, self.act, self.ye,
-                        h13=self.h13, stream=stream)
+        keep = self.backward_enabled and not self.lean
+        xmoe_expert_ffn_gather(x, self.pft.token_ids, w["w1"], w["w3"], w["w2"], self.pft.expert_offsets,
+                               self.act, self.ye, h13=self.h13 if keep else None, stream=stream)
         mark("expert_ffn")
         y_add = None
         if self.shared:
             s1, s3, s2 = self._shared_w()
-            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y, h13=self.sh_h13, stream=stream)
+            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y,
+                            h13=self.sh_h13 if keep else None, stream=stream)
             mark("shared_ffn")
             y_add = self.sh_y
         xmoe_combine(self.ye, self.pft, self.T, self.y, y_add=y_add, stream=stream)
@@ -110,6 +120,13 @@ class PaddingFreeMoE:
         mark = hook or (lambda name: None)
         xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w, stream=stream)
         mark("combine_bwd")
+        if self.lean:
+            # recompute the pre-activations (act is rewritten with the same values)
+            xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, w["w1"], w["w3"], self.pft.expert_offsets,
+                                      self.act, self.h13, stream=stream)
+            mark("recompute_h13")
+        xmoe_dispatch(self.x, self.k, self.pft, self.xs, stream=stream)
+        mark("dispatch")
         xmoe_expert_ffn_bwd(self.xs, w["w1"], w["w3"], w["w2"], self.act, self.h13, self.dye,
                             self.pft.expert_offsets, self.dh13, self.dxs, self.dw1, self.dw3, self.dw2,
                             stream=stream)
@@ -117,6 +134,9 @@ class PaddingFreeMoE:
         dx_add = None
         if self.shared:
             s1, s3, s2 = self._shared_w()
+            if self.lean:
+                xmoe_expert_ffn_up(self.x, s1, s3, self.sh_off, self.sh_act, self.sh_h13, stream=stream)
+                mark("recompute_shared_h13")
             xmoe_expert_ffn_bwd(self.x, s1, s3, s2, self.sh_act, self.sh_h13, dy, self.sh_off, self.sh_dh13,
                                 self.sh_dx, self.ds1, self.ds3, self.ds2, stream=stream)
             mark("shared_ffn_bwd")
@@ -127,6 +147,19 @@ class PaddingFreeMoE:
                        self.rbwd_ws, self.inv_tau, stream=stream)
         mark("route_bwd")
         return self.dx
+
+    def saved_bytes(self) -> int:
+        """Bytes the backward needs from the forward (beyond x and the weights):
+        routing results, the PFT, act and ye, plus H1/H3 unless lean."""
+        def nb(t):
+            return 0 if t is None else t.numel() * t.element_size()
+        n = nb(self.topk_ids) + nb(self.topk_w) + nb(self.logits) + nb(self.act) + nb(self.ye)
+        n += sum(nb(t) for t in self.pft.fields().values())
+        if not self.lean:
+            n += nb(self.h13)
+        if self.shared:
+            n += nb(self.sh_act) + (0 if self.lean else nb(self.sh_h13))
+        return n
 
     def grads(self) -> Dict[str, torch.Tensor]:
         g = {"dx": self.dx, "dwg": self.dwg, "dw1": self.dw1, "dw3": self.dw3, "dw2": self.dw2,

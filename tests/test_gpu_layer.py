@@ -38,22 +38,24 @@ def _oracle_inputs(inp):
     return out
 
 
-def run_layer(xm, wl, inp):
+def run_layer(xm, wl, inp, lean=False):
     from padding_free_expert_amd.layer import PaddingFreeMoE
     g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     weights = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g}
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True)
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean)
     layer.forward(g["x"])
     layer.backward(g["dy"])
     torch.cuda.synchronize()
     return layer
 
 
+@pytest.mark.parametrize("lean", [False, True], ids=["saved-h13", "lean"])
 @pytest.mark.parametrize("name", NAMES)
-def test_layer_forward_backward(xm, name):
+def test_layer_forward_backward(xm, name, lean):
+    """lean=True recomputes H1/H3 in the backward instead of keeping them."""
     wl = workloads.small(name)
     inp = workloads.generate(wl, backward=True)
-    layer = run_layer(xm, wl, inp)
+    layer = run_layer(xm, wl, inp, lean=lean)
     o = _oracle_inputs(inp)
     mode = 0 if wl.dtype == "f32" else 1
     fwd = orc.layer_forward(o, wl.k, mode, wl.inv_tau, n_shared=wl.n_shared)
@@ -137,6 +139,20 @@ def test_layer_forward_backward(xm, name):
     # experts no token chose get an explicit zero gradient
     for e in np.nonzero(pft["tokens_per_expert"] == 0)[0]:
         assert (layer.dw1[e] == 0).all() and (layer.dw3[e] == 0).all() and (layer.dw2[e] == 0).all()
+
+
+def test_lean_layer_matches_saved_layer_bitwise(xm):
+    """Recomputing H1/H3 runs the same kernel on the same inputs, so the lean
+    layer's outputs and gradients are bitwise those of the layer that keeps
+    them; it also keeps fewer bytes from the forward."""
+    wl = workloads.small("dsmoe16b")
+    inp = workloads.generate(wl, backward=True)
+    a = run_layer(xm, wl, inp, lean=False)
+    b = run_layer(xm, wl, inp, lean=True)
+    for key, ga in a.grads().items():
+        assert torch.equal(ga, b.grads()[key]), key
+    assert torch.equal(a.y, b.y)
+    assert b.saved_bytes() < a.saved_bytes()
 
 
 def test_layer_is_deterministic(xm):

@@ -227,6 +227,54 @@ def test_expert_ffn_forward(xm, dtype, rows, d, h, E, empty):
     assert_close(host(ye), ref["ye"], rt, "ye")
 
 
+GATHER_CASES = [
+    ("f32", 97, 64, 40, 5, 2, 0.0),
+    ("bf16", 300, 256, 200, 16, 6, 1.5),   # skewed: some experts empty
+    ("bf16", 517, 328, 264, 7, 3, 0.7),    # d and h off every tile multiple
+    ("bf16", 129, 128, 128, 1, 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("dtype,T,d,h,E,k,skew", GATHER_CASES)
+def test_expert_ffn_gather(xm, dtype, T, d, h, E, k, skew):
+    """The FFN with the dispatch gather fused into the up-projection's loads,
+    on expert-sorted rows built by the oracle's PFT, against the oracle's FFN
+    over the same token-to-row map."""
+    ids, w = workloads.random_topk(T, E, k, seed=T + d, skew=skew)
+    ref_pft = orc.build_pft(ids.numpy(), w.numpy(), E)
+    tok, off = ref_pft["token_ids"], ref_pft["expert_offsets"]
+    R = T * k
+    row_expert = np.repeat(np.arange(E, dtype=np.int32), np.diff(off))
+    x = workloads.random_rows(T, d, dtype, seed=T + 7)
+    g = torch.Generator().manual_seed(T + d)
+    tdt = DT[dtype]
+    w1 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w3 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w2 = (torch.randn((E, h, d), generator=g) / h ** 0.5).to(tdt)
+    c = lambda t: t.cuda()
+    tok_d, off_d = torch.from_numpy(tok).cuda(), torch.from_numpy(off).cuda()
+    act = torch.empty((R, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((R, 2 * h), dtype=tdt, device="cuda")
+    ye = torch.empty((R, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_gather(c(x), tok_d, c(w1), c(w3), c(w2), off_d, act, ye, h13=h13)
+    ref = orc.ffn(orc_in(x), row_expert, orc_in(w1), orc_in(w3), orc_in(w2), row_token=tok, want_hidden=True)
+    rt = RTOL[dtype]
+    hh = host(h13)
+    assert_close(hh[:, :h], ref["h1"], rt, "h1")
+    assert_close(hh[:, h:], ref["h3"], rt, "h3")
+    assert_close(host(act), ref["act"], rt, "act")
+    assert_close(host(ye), ref["ye"], rt, "ye")
+    # consistency with the materialised path (same arithmetic, so bitwise)
+    xs = c(x)[tok_d.long()].contiguous()
+    act2, h132, ye2 = torch.empty_like(act), torch.empty_like(h13), torch.empty_like(ye)
+    xm.xmoe_expert_ffn(xs, c(w1), c(w3), c(w2), off_d, act2, ye2, h13=h132)
+    assert torch.equal(act, act2) and torch.equal(h13, h132) and torch.equal(ye, ye2)
+    # up-projection alone, without the saved pre-activations
+    act3 = torch.empty_like(act)
+    xm.xmoe_expert_ffn_up_gather(c(x), tok_d, c(w1), c(w3), off_d, act3)
+    assert torch.equal(act3, act)
+
+
 @pytest.mark.parametrize("dtype,rows,d,h,E,empty", FFN_CASES)
 def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
     off, xs, w1, w3, w2, re_ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=rows + 2 * d)
