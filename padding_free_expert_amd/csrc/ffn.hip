@@ -7,7 +7,8 @@
 // and the expert count, and each block finds its expert and row tile from the
 // device-side offsets (see gemm.hpp).  The bf16 products run on the pipelined
 // LDS-DMA kernel; tile shapes were chosen per product by timing on MI355X
-// (BM x BN x BK, NB weight matrices, S ring slots, blocks per compute unit).  The expert is a SwiGLU FFN (a reading:
+// (BM x BN x BK, wave grid, NB weight matrices, S ring slots, blocks per
+// compute unit), comparing candidates within one run on one device.  The expert is a SwiGLU FFN (a reading:
 // the pages name no FFN form), so the up-projection multiplies the same rows
 // by W1 and W3 in one kernel and applies silu(H1) * H3 in its epilogue.
 //
@@ -35,6 +36,17 @@ GemmArgs rows_args(const int32_t *offsets, int E, int64_t rows) {
     p.extent = rows;
     p.nphase = 1;
     return p;
+}
+
+// Large tiles (256-row, eight waves) cut the bytes each product moves from L2
+// into LDS by a third, but they round every expert's rows up to a multiple of
+// 256 and need enough tiles to fill the device.  They are used when the
+// average group has at least 1024 rows and the large-tile grid still gives two
+// blocks per compute unit; otherwise the 128-row, two-blocks-per-CU tiles.
+bool large_tiles(int64_t rows, int E, int64_t n, int bn) {
+    const int64_t per_group = rows / (E > 0 ? E : 1);
+    const int64_t tiles = (rows / 256 + E) * ((n + bn - 1) / bn);
+    return per_group >= 1024 && tiles >= 512;
 }
 
 GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
@@ -68,8 +80,9 @@ hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t
     p.aux_out = h13;
     p.ld_aux = 2 * static_cast<int64_t>(h);
     p.hoff = h;
-    return dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, true, false, 3, EPI_SWIGLU, bf16_t, 2>(p, s)
-                       : launch_gemm_f32<2, true, false, EPI_SWIGLU>(p, s);
+    if (dt != kBF16) return launch_gemm_f32<2, true, false, EPI_SWIGLU>(p, s);
+    return large_tiles(rows, E, h, 128) ? launch_gemm_dma<256, 128, 32, 4, 2, 2, true, false, 4, EPI_SWIGLU, bf16_t, 1>(p, s)
+                                       : launch_gemm_dma<128, 128, 32, 2, 2, 2, true, false, 3, EPI_SWIGLU, bf16_t, 2>(p, s);
 }
 
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows, int d,
@@ -84,8 +97,9 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
     p.b_gstride = static_cast<int64_t>(h) * d;
     p.C0 = ye;
     p.ldc = d;
-    return dt == kBF16 ? launch_gemm_dma<128, 256, 32, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s)
-                       : launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
+    if (dt != kBF16) return launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
+    return large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                       : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
 }
 
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
@@ -108,8 +122,9 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.aux = h13;
         p.ld_aux = 2 * static_cast<int64_t>(h);
         p.hoff = h;
-        err = dt == kBF16 ? launch_gemm_dma<128, 128, 64, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s)
-                          : launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s);
+        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
+              : large_tiles(rows, E, h, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
+                                             : launch_gemm_dma<128, 128, 64, 2, 2, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
         if (err != hipSuccess) return err;
     }
     {   // dxs = dH1 . W1[e]^T + dH3 . W3[e]^T
@@ -126,8 +141,9 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.b_gstride = dh;
         p.C0 = dxs;
         p.ldc = d;
-        err = dt == kBF16 ? launch_gemm_dma<256, 256, 32, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
-                          : launch_gemm_f32<1, true, true, EPI_STORE>(p, s);
+        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(p, s)
+              : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                             : launch_gemm_dma<256, 256, 32, 2, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
         if (err != hipSuccess) return err;
     }
     {   // dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert)
@@ -143,7 +159,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.Cx = dw3;
         p.ldc = h;
         p.c_gstride = dh;
-        err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
+        err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
                           : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
         if (err != hipSuccess) return err;
     }
@@ -158,8 +174,9 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
         p.C0 = dw2;
         p.ldc = d;
         p.c_gstride = dh;
-        err = dt == kBF16 ? launch_gemm_dma<128, 256, 32, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
-                          : launch_gemm_f32<1, false, false, EPI_STORE>(p, s);
+        err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(p, s)
+              : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, false, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                             : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
     }
     return err;
 }

@@ -682,22 +682,23 @@ __device__ __forceinline__ int swz_mn(int k, int cpr) {
 }
 
 // Per-thread load plan of one operand tile (R mn x BK k), the same for every
-// stage: 256 threads x 16 bytes per instruction, kN instructions per thread.
-template <int R, int BK, bool KC>
+// stage: NW waves x 64 lanes x 16 bytes per instruction, kN instructions per
+// thread; instruction i of wave w fills the tile's 1 KiB block i*NW + w.
+template <int R, int BK, bool KC, int NW>
 struct DmaPlan {
     static constexpr int kRowBytes = KC ? BK * 2 : R * 2;
     static constexpr int kCpr = kRowBytes / 16;
     static constexpr int kBytes = R * BK * 2;
-    static constexpr int kN = kBytes / 4096;
-    static_assert(kBytes % 4096 == 0, "operand tile must be a multiple of 4 KiB");
-    static_assert(KC ? (BK == 32 || BK == 64) : (R == 64 || R == 128 || R == 256), "unsupported tile");
+    static constexpr int kN = kBytes / (NW * 1024);
+    static_assert(kBytes % (NW * 1024) == 0, "operand tile must be a whole number of block-wide loads");
+    static_assert(KC ? (BK == 32 || BK == 64) : (R == 64 || R == 128 || R == 256 || R == 512), "unsupported tile");
     int base[kN];  // byte offset of this lane's chunk at the stage's first k
     int lim[kN];   // the chunk is in range iff k0 < lim (INT_MIN: row/column out of range)
     // KC: rows r < rmax (r relative to the tile); MN: columns r0 + 8c < rmax
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int r0, int rmax, int kmax) {
 #pragma unroll
         for (int i = 0; i < kN; ++i) {
-            const int o = (i * 4 + wave) * 1024 + lane * 16;
+            const int o = (i * NW + wave) * 1024 + lane * 16;
             const int row = o / kRowBytes, s = (o % kRowBytes) / 16;
             if constexpr (KC) {
                 const int c = s ^ swz_kc(row, kCpr);
@@ -716,7 +717,7 @@ struct DmaPlan {
         static_assert(KC, "row maps apply to k-contiguous operands");
 #pragma unroll
         for (int i = 0; i < kN; ++i) {
-            const int o = (i * 4 + wave) * 1024 + lane * 16;
+            const int o = (i * NW + wave) * 1024 + lane * 16;
             const int row = o / kRowBytes, s = (o % kRowBytes) / 16;
             const int c = s ^ swz_kc(row, kCpr);
             const int64_t mr = row < rmax ? rmap[row] : 0;
@@ -728,7 +729,7 @@ struct DmaPlan {
     // KC: kadd = 2*k0; MN: the buffer starts at the block's first k row
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kc, int kadd, uint32_t dst, int wave,
                                           int i) const {
-        lds_dma16(rs, kc < lim[i] ? base[i] + kadd : kOob, dst + (i * 4 + wave) * 1024);
+        lds_dma16(rs, kc < lim[i] ? base[i] + kadd : kOob, dst + (i * NW + wave) * 1024);
     }
 };
 
@@ -754,22 +755,30 @@ struct FragAddr {
     }
 };
 
-// BM x (NB*BN) output tile per 256-thread block (2 x 2 waves), BK-deep k
-// blocks on an S-slot LDS ring.  Per k step (16 of k) each wave issues its
-// NB*TN*TM matrix-core products interleaved with the fragment reads of the next
-// step (two register sets) and with its share of the loads of the block S-1
-// ahead.  The barrier of block `it` sits at the start of its last k step: all
+// BM x (NB*BN) output tile per block of WGM x WGN waves, BK-deep k blocks on
+// an S-slot LDS ring.  Per k step (16 of k) each wave issues its NB*TN*TM
+// matrix-core products interleaved with the fragment reads of the next step
+// (two register sets) and with its share of the loads of the block S-1 ahead.
+// The barrier of block `it` sits at the start of its last k step: all
 // fragments of the block are in registers by then, so the freed slot can be
 // refilled and the next block's first fragments read while the last products
-// of this block run.  OCC = 2 keeps LDS and registers low enough for two blocks
-// per compute unit.
-template <int BM, int BN, int BK, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT, int OCC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_dma_kernel(GemmArgs p) {
-    constexpr int WTM = BM / 2, WTN = BN / 2;
+// of this block run.  OCC = 2 keeps LDS and registers low enough for two
+// blocks per compute unit; 8 waves put two waves of one block on each SIMD.
+// A wave whose rows (or columns) all lie past the group's end skips its
+// products and fragment reads (it still loads and meets every barrier), so
+// the ragged last row tile of an expert costs matrix-core time only for its
+// valid wave rows.
+template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT,
+          int OCC>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
+void gemm_dma_kernel(GemmArgs p) {
+    constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be a multiple of 32");
-    using PA = DmaPlan<BM, BK, A_KC>;
-    using PB = DmaPlan<BN, BK, B_KC>;
+    using PA = DmaPlan<BM, BK, A_KC, NW>;
+    using PB = DmaPlan<BN, BK, B_KC, NW>;
     constexpr int kABytes = PA::kBytes, kBBytes = PB::kBytes;
     constexpr int kStage = kABytes + NB * kBBytes;
     constexpr int kL = PA::kN + NB * PB::kN;   // loads per thread per k block
@@ -789,8 +798,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int m0 = t.mt * BM, n0 = t.nt * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    const bool wact = m0 + wm * WTM < t.Mg && n0 + wn * WTN < p.N;  // this wave has output
 
     const int ktiles = (t.Kg + BK - 1) / BK;
     const int nph = p.group_mode == GM_KSPLIT ? 1 : p.nphase;
@@ -914,49 +924,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
     wait_vmem<kL * (S - 2)>();
     __syncthreads();
+    // The k loop, instantiated for waves with output (products and fragment
+    // reads) and without (loads and barriers only); both meet the same barriers.
+    auto k_loop = [&](auto active) {
+        constexpr bool ACT = decltype(active)::value;
+        if constexpr (ACT) {
 #pragma unroll
-    for (int u = 0; u < NR; ++u) read_unit(0, u, sbase, 0);
-
-    int cur = 0;  // ring slot of block `it`
-    for (int it = 0; it < total; ++it) {
-        const uint32_t sa = sbase + cur * kStage;
-        const int nxt = cur + 1 == S ? 0 : cur + 1;
-        const uint32_t sf = sbase + (cur == 0 ? S - 1 : cur - 1) * kStage;  // freed by the last barrier
-        const StagePlan sp = plan_stage(it + S - 1);
+            for (int u = 0; u < NR; ++u) read_unit(0, u, sbase, 0);
+        }
+        int cur = 0;  // ring slot of block `it`
+        for (int it = 0; it < total; ++it) {
+            const uint32_t sa = sbase + cur * kStage;
+            const int nxt = cur + 1 == S ? 0 : cur + 1;
+            const uint32_t sf = sbase + (cur == 0 ? S - 1 : cur - 1) * kStage;  // freed by the last barrier
+            const StagePlan sp = plan_stage(it + S - 1);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int c = kk & 1, n = c ^ 1;
-            uint32_t rs = sa;
-            int rk = kk + 1;
-            if (kk == KK - 1) {
-                wait_vmem<kL * (S - 2)>();  // this wave's loads of block it+1 have landed
-                __syncthreads();            // ... everyone's, and all reads of block it are done
-                rs = sbase + nxt * kStage;
-                rk = 0;
-            }
-#pragma unroll
-            for (int qq = 0; qq < NM; ++qq) {
-                const int b = qq / (TN * TM), j = (qq / TM) % TN, i = qq % TM;
-                acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fB[c][b][j], fA[c][i], acc[b][i][j], 0, 0, 0);
-                if (qq < NR) read_unit(n, qq, rs, rk * 16);
-                if (qq == NM - 1) {
-#pragma unroll
-                    for (int u = NM; u < NR; ++u) read_unit(n, u, rs, rk * 16);
+            for (int kk = 0; kk < KK; ++kk) {
+                const int c = kk & 1, n = c ^ 1;
+                uint32_t rs = sa;
+                int rk = kk + 1;
+                if (kk == KK - 1) {
+                    wait_vmem<kL * (S - 2)>();  // this wave's loads of block it+1 have landed
+                    __syncthreads();            // ... everyone's, and all reads of block it are done
+                    rs = sbase + nxt * kStage;
+                    rk = 0;
                 }
-                if (kk < KK - 1) {
 #pragma unroll
-                    for (int z = 0; z < DPQ; ++z) {
-                        const int part = kk * DPK + qq * DPQ + z;
-                        if (qq * DPQ + z < DPK && part < kL) issue_part(sp, sf, part);
+                for (int qq = 0; qq < NM; ++qq) {
+                    if constexpr (ACT) {
+                        const int b = qq / (TN * TM), j = (qq / TM) % TN, i = qq % TM;
+                        acc[b][i][j] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fB[c][b][j], fA[c][i], acc[b][i][j], 0, 0, 0);
+                        if (qq < NR) read_unit(n, qq, rs, rk * 16);
+                        if (qq == NM - 1) {
+#pragma unroll
+                            for (int u = NM; u < NR; ++u) read_unit(n, u, rs, rk * 16);
+                        }
+                    }
+                    if (kk < KK - 1) {
+#pragma unroll
+                        for (int z = 0; z < DPQ; ++z) {
+                            const int part = kk * DPK + qq * DPQ + z;
+                            if (qq * DPQ + z < DPK && part < kL) issue_part(sp, sf, part);
+                        }
                     }
                 }
-#ifdef XMOE_GEMM_PIN_ORDER
-                __builtin_amdgcn_sched_barrier(0);
-#endif
             }
+            cur = nxt;
         }
-        cur = nxt;
-    }
+    };
+    if (wact) k_loop(std::true_type{});
+    else k_loop(std::false_type{});
     wait_vmem<0>();  // no load may still target LDS when the block ends
 
     // accumulator (i, j, r) of lane l holds C[row, col] with
@@ -969,7 +987,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         // (16 lanes per 256-byte row segment) instead of 8-byte pieces.
         constexpr int LDC = BN + 8;
         // two passes (one per row half, i.e. per wave row) when the tile does not fit the ring
-        constexpr int kPass = BM * LDC * 2 <= S * kStage ? 1 : 2;
+        constexpr int kPass = BM * LDC * 2 <= S * kStage ? 1 : WGM;  // 1 pass, or one per wave row
         constexpr int RP = BM / kPass;  // rows per pass
         static_assert(RP * LDC * 2 <= S * kStage, "output tile must fit the ring");
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
@@ -1014,7 +1032,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
                 }
                 __syncthreads();
 #pragma unroll 4
-                for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+                for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
                     const int row = c / (BN / 8), c8 = c % (BN / 8);
                     const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
                     if (m < t.Mg && n < p.N)
@@ -1032,7 +1050,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         // the same places into dH1/dH3 in place, and both tiles leave in
         // 16-byte row chunks.
         constexpr int LDC = BN + 8;
-        constexpr int kPass = 2 * BM * LDC * 2 <= S * kStage ? 1 : 2;
+        constexpr int kPass = 2 * BM * LDC * 2 <= S * kStage ? 1 : WGM;
         constexpr int RP = BM / kPass;
         static_assert(2 * RP * LDC * 2 <= S * kStage, "H1/H3 tiles must fit the ring");
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
@@ -1043,7 +1061,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         __syncthreads();  // every wave is done with the ring
         for (int pass = 0; pass < kPass; ++pass) {
 #pragma unroll 4
-            for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+            for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
                 const int row = c / (BN / 8), c8 = c % (BN / 8);
                 const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
                 if (m < t.Mg && n < p.N) {
@@ -1080,7 +1098,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
             }
             __syncthreads();
 #pragma unroll 4
-            for (int c = threadIdx.x; c < RP * BN / 8; c += 256) {
+            for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
                 const int row = c / (BN / 8), c8 = c % (BN / 8);
                 const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
                 if (m < t.Mg && n < p.N) {
@@ -1115,12 +1133,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     }
 }
 
-template <int BM, int BN, int BK, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT, int OCC>
+template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT,
+          int OCC>
 inline hipError_t launch_gemm_dma(const GemmArgs &p, hipStream_t stream) {
     const int64_t grid = gemm_grid<BM, BN>(p);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, NB, A_KC, B_KC, S, EPI, OutT, OCC>),
-                       dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WGM, WGN, NB, A_KC, B_KC, S, EPI, OutT, OCC>),
+                       dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
 
