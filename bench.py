@@ -180,7 +180,7 @@ def main():
         tot_ms += t
         tot_flop += fl
     achieved = tot_flop / (tot_ms * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_dma_kernel<256,128,32,4,2,2,...,EPI_SWIGLU> (expert up-projection)",
+    roofline = {"kernel": "gemm_dma_kernel<128,128,32,2,2,2,...,EPI_SWIGLU> (expert up-projection, DeepSeek-MoE-16B tile)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                 "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches)}
