@@ -33,7 +33,7 @@ class PaddingFreeMoE:
     the backward needs from the forward shrinks to act, ye and the routing."""
 
     def __init__(self, weights: Dict[str, torch.Tensor], T: int, k: int, inv_tau: float = 1.0,
-                 backward: bool = True, lean: bool = False):
+                 backward: bool = True, lean: bool = False, overlap: bool = True):
         self.w = weights
         wg, w1 = weights["wg"], weights["w1"]
         self.dtype = wg.dtype
@@ -44,6 +44,10 @@ class PaddingFreeMoE:
         self.shared = weights.get("s1") is not None
         self.backward_enabled = backward
         self.lean = lean
+        # the shared experts depend only on x (forward) and dy (backward): with
+        # overlap they run on a second stream (default priority) beside the
+        # routed path and fill the tail of its GEMMs
+        self.overlap = overlap
         dev, dt = self.device, self.dtype
         T, d, E, h, R = T, self.d, self.E, self.h, T * k
         f32 = dict(dtype=torch.float32, device=dev)
@@ -65,6 +69,7 @@ class PaddingFreeMoE:
             self.sh_act = torch.empty((T, hs), dtype=dt, device=dev)
             self.sh_h13 = torch.empty((T, 2 * hs), dtype=dt, device=dev) if backward else None
             self.sh_y = torch.empty((T, d), dtype=dt, device=dev)
+            self.side = torch.cuda.Stream(device=dev)
         if backward:
             self.dtopk_w = torch.empty((T, k), **f32)
             self.dye = torch.empty((R, d), dtype=dt, device=dev)
@@ -90,27 +95,37 @@ class PaddingFreeMoE:
         w = self.w
         return w["s1"].unsqueeze(0), w["s3"].unsqueeze(0), w["s2"].unsqueeze(0)
 
+    def _streams(self, stream):
+        main = stream if stream is not None else torch.cuda.current_stream(self.device)
+        side = self.side if (self.shared and self.overlap) else main
+        return main, side
+
     def forward(self, x: torch.Tensor, stream=None, hook=None) -> torch.Tensor:
         """hook(name), if given, is called after each library call is enqueued."""
         w = self.w
         mark = hook or (lambda name: None)
-        xmoe_route(x, w["wg"], self.k, self.topk_ids, self.topk_w, self.logits, self.inv_tau,
-                   w.get("logit_bias"), w.get("select_bias"), stream=stream)
-        mark("route")
-        xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=stream)
-        mark("build_pft")
+        main, side = self._streams(stream)
         keep = self.backward_enabled and not self.lean
+        if self.shared:
+            side.wait_stream(main)
+            s1, s3, s2 = self._shared_w()
+            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y,
+                            h13=self.sh_h13 if keep else None, stream=side)
+            if side is main:
+                mark("shared_ffn")
+        xmoe_route(x, w["wg"], self.k, self.topk_ids, self.topk_w, self.logits, self.inv_tau,
+                   w.get("logit_bias"), w.get("select_bias"), stream=main)
+        mark("route")
+        xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=main)
+        mark("build_pft")
         xmoe_expert_ffn_gather(x, self.pft.token_ids, w["w1"], w["w3"], w["w2"], self.pft.expert_offsets,
-                               self.act, self.ye, h13=self.h13 if keep else None, stream=stream)
+                               self.act, self.ye, h13=self.h13 if keep else None, stream=main)
         mark("expert_ffn")
         y_add = None
         if self.shared:
-            s1, s3, s2 = self._shared_w()
-            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y,
-                            h13=self.sh_h13 if keep else None, stream=stream)
-            mark("shared_ffn")
+            main.wait_stream(side)
             y_add = self.sh_y
-        xmoe_combine(self.ye, self.pft, self.T, self.y, y_add=y_add, stream=stream)
+        xmoe_combine(self.ye, self.pft, self.T, self.y, y_add=y_add, stream=main)
         mark("combine")
         self.x = x
         return self.y
@@ -118,33 +133,39 @@ class PaddingFreeMoE:
     def backward(self, dy: torch.Tensor, stream=None, hook=None) -> torch.Tensor:
         w = self.w
         mark = hook or (lambda name: None)
-        xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w, stream=stream)
+        main, side = self._streams(stream)
+        dx_add = None
+        if self.shared:
+            side.wait_stream(main)
+            s1, s3, s2 = self._shared_w()
+            if self.lean:
+                xmoe_expert_ffn_up(self.x, s1, s3, self.sh_off, self.sh_act, self.sh_h13, stream=side)
+                if side is main:
+                    mark("recompute_shared_h13")
+            xmoe_expert_ffn_bwd(self.x, s1, s3, s2, self.sh_act, self.sh_h13, dy, self.sh_off, self.sh_dh13,
+                                self.sh_dx, self.ds1, self.ds3, self.ds2, stream=side)
+            if side is main:
+                mark("shared_ffn_bwd")
+            dx_add = self.sh_dx
+        xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w, stream=main)
         mark("combine_bwd")
         if self.lean:
             # recompute the pre-activations (act is rewritten with the same values)
             xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, w["w1"], w["w3"], self.pft.expert_offsets,
-                                      self.act, self.h13, stream=stream)
+                                      self.act, self.h13, stream=main)
             mark("recompute_h13")
-        xmoe_dispatch(self.x, self.k, self.pft, self.xs, stream=stream)
+        xmoe_dispatch(self.x, self.k, self.pft, self.xs, stream=main)
         mark("dispatch")
         xmoe_expert_ffn_bwd(self.xs, w["w1"], w["w3"], w["w2"], self.act, self.h13, self.dye,
                             self.pft.expert_offsets, self.dh13, self.dxs, self.dw1, self.dw3, self.dw2,
-                            stream=stream)
+                            stream=main)
         mark("expert_ffn_bwd")
-        dx_add = None
         if self.shared:
-            s1, s3, s2 = self._shared_w()
-            if self.lean:
-                xmoe_expert_ffn_up(self.x, s1, s3, self.sh_off, self.sh_act, self.sh_h13, stream=stream)
-                mark("recompute_shared_h13")
-            xmoe_expert_ffn_bwd(self.x, s1, s3, s2, self.sh_act, self.sh_h13, dy, self.sh_off, self.sh_dh13,
-                                self.sh_dx, self.ds1, self.ds3, self.ds2, stream=stream)
-            mark("shared_ffn_bwd")
-            dx_add = self.sh_dx
-        xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=stream)
+            main.wait_stream(side)
+        xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=main)
         mark("dispatch_bwd")
         xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.dx, self.dwg,
-                       self.rbwd_ws, self.inv_tau, stream=stream)
+                       self.rbwd_ws, self.inv_tau, stream=main)
         mark("route_bwd")
         return self.dx
 

@@ -38,11 +38,11 @@ def _oracle_inputs(inp):
     return out
 
 
-def run_layer(xm, wl, inp, lean=False):
+def run_layer(xm, wl, inp, lean=False, overlap=True):
     from padding_free_expert_amd.layer import PaddingFreeMoE
     g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     weights = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g}
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean)
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean, overlap=overlap)
     layer.forward(g["x"])
     layer.backward(g["dy"])
     torch.cuda.synchronize()
@@ -153,6 +153,18 @@ def test_lean_layer_matches_saved_layer_bitwise(xm):
         assert torch.equal(ga, b.grads()[key]), key
     assert torch.equal(a.y, b.y)
     assert b.saved_bytes() < a.saved_bytes()
+
+
+def test_side_stream_matches_serial_bitwise(xm):
+    """The shared experts on their own stream give bitwise the results of the
+    serial call order (the stream waits carry every dependency)."""
+    wl = workloads.small("dsmoe16b")
+    inp = workloads.generate(wl, backward=True)
+    a = run_layer(xm, wl, inp, overlap=False)
+    b = run_layer(xm, wl, inp, overlap=True)
+    assert torch.equal(a.y, b.y)
+    for key, ga in a.grads().items():
+        assert torch.equal(ga, b.grads()[key]), key
 
 
 def test_layer_is_deterministic(xm):
