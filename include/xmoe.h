@@ -114,12 +114,20 @@ xmoe_status xmoe_query_device(int ordinal, int *is_gfx950);
  * it is the softmax input the backward needs.  With XMOE_F32 each logit is one
  * fused multiply-add per feature in ascending order; with XMOE_BF16 the sum
  * runs on bf16 matrix cores with fp32 accumulation.
+ * With XMOE_BF16 the reduction over d is split into a few ranges whose fp32
+ * partial sums go to `workspace` (caller-owned device memory of at least
+ * xmoe_route_workspace_size bytes, 16-byte aligned, no initialisation needed,
+ * dead after the call) and are added in range order, so the result is
+ * deterministic; XMOE_F32 needs no workspace (it may be NULL).
  * Limits: 1 <= k <= E <= 1024, d >= 1; bf16 needs d % 8 == 0 and E % 8 == 0.
  */
 xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t T, int32_t d,
                        int32_t E, int32_t k, float inv_temperature, const float *logit_bias,
                        const float *select_bias, int32_t *topk_ids, float *topk_w, float *logits,
-                       void *stream);
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes xmoe_route needs for these sizes (0: none needed, or invalid). */
+size_t xmoe_route_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype dtype);
 
 /* Workspace bytes xmoe_build_pft needs for these sizes (0 if invalid). */
 size_t xmoe_build_pft_workspace_size(int64_t T, int32_t E, int32_t k);

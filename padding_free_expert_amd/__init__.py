@@ -16,6 +16,7 @@ import torch
 
 __all__ = [
     "XmoeError", "PFT", "lib_path", "xmoe_version", "xmoe_query_device", "xmoe_route",
+    "xmoe_route_workspace_size",
     "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
@@ -53,7 +54,8 @@ _lib_last_error = _sig("xmoe_last_error", [], ctypes.c_char_p)
 _lib_version = _sig("xmoe_version", [])
 _lib_query = _sig("xmoe_query_device", [ctypes.c_int, ctypes.POINTER(ctypes.c_int)])
 _lib_route = _sig("xmoe_route", [_vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
-                                 _vp, _vp])
+                                 _vp, _vp, _sz, _vp])
+_lib_route_ws = _sig("xmoe_route_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
 _lib_pft_ws = _sig("xmoe_build_pft_workspace_size", [_i64, _i32, _i32], _sz)
 _lib_pft = _sig("xmoe_build_pft", [_vp, _vp, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _sz, _vp])
 _lib_dispatch = _sig("xmoe_dispatch", [_vp, ctypes.c_int, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _vp])
@@ -151,12 +153,23 @@ def xmoe_query_device(ordinal: int = 0) -> bool:
     return bool(v.value)
 
 
+def xmoe_route_workspace_size(T: int, d: int, E: int, dtype) -> int:
+    return int(_lib_route_ws(T, d, E, XMOE_BF16 if dtype == torch.bfloat16 else XMOE_F32))
+
+
 def xmoe_route(x, wg, k: int, topk_ids, topk_w, logits, inv_temperature: float = 1.0,
-               logit_bias=None, select_bias=None, stream=None):
+               logit_bias=None, select_bias=None, workspace=None, stream=None):
+    """workspace: device tensor of at least xmoe_route_workspace_size bytes; allocated
+    here (torch) when None."""
     T, d = x.shape
     E = wg.shape[1]
+    need = xmoe_route_workspace_size(T, d, E, x.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib_route(_ptr(x), _ptr(wg), _dt(x), T, d, E, k, inv_temperature, _ptr(logit_bias),
-                      _ptr(select_bias), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _stream(stream)),
+                      _ptr(select_bias), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(workspace), nbytes,
+                      _stream(stream)),
            "xmoe_route")
 
 

@@ -145,9 +145,14 @@ xmoe_status xmoe_query_device(int ordinal, int *is_gfx950) {
     return ok();
 }
 
+size_t xmoe_route_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype dtype) {
+    if (T < 0 || d < 1 || E < 1 || E > 1024 || (dtype != XMOE_BF16 && dtype != XMOE_F32)) return 0;
+    return xmoe::route_workspace(T, d, E, dtype);
+}
+
 xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t T, int32_t d, int32_t E, int32_t k,
                        float inv_temperature, const float *logit_bias, const float *select_bias, int32_t *topk_ids,
-                       float *topk_w, float *logits, void *stream) {
+                       float *topk_w, float *logits, void *workspace, size_t ws_bytes, void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(wg && (T == 0 || (x && topk_ids && topk_w && logits)), XMOE_ERR_INVALID_VALUE,
             "a required pointer is NULL");
@@ -159,9 +164,13 @@ xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t 
         REQUIRE(d % 8 == 0 && E % 8 == 0, XMOE_ERR_UNSUPPORTED, "bf16 routing needs d and E multiples of 8");
         REQUIRE(aligned16(x) && aligned16(wg), XMOE_ERR_UNSUPPORTED, "x and wg must be 16-byte aligned");
     }
+    const size_t need = xmoe::route_workspace(T, d, E, dtype);
+    REQUIRE(need == 0 || (workspace && aligned16(workspace)), XMOE_ERR_WORKSPACE,
+            "workspace is NULL or not 16-byte aligned");
+    REQUIRE(ws_bytes >= need, XMOE_ERR_WORKSPACE, "workspace too small (see xmoe_route_workspace_size)");
     CHECK_DEVICE();
     return hip_status(xmoe::launch_route(dtype, x, wg, T, d, E, k, inv_temperature, logit_bias, select_bias, topk_ids,
-                                         topk_w, logits, S(stream)),
+                                         topk_w, logits, workspace, S(stream)),
                       "xmoe_route launch");
 }
 

@@ -56,6 +56,11 @@ struct GemmArgs {
     // a_map_rows rows), i.e. the dispatch gather happens in the operand loads.
     const int32_t *a_map;
     int64_t a_map_rows;
+    // GM_ROWS split over k (pipelined kernel only): block b works on k range
+    // part b % kparts of length kpart_len and writes C + part * c_gstride
+    // (partial sums, EPI_STORE); kparts <= 1 means no split.
+    int kparts;
+    int kpart_len;
 };
 
 // ---------------------------------------------------------------- epilogues
@@ -144,12 +149,12 @@ __device__ __forceinline__ int xcd_tile_order(int b, int nblocks) {
 // GM_ROWS: the group is located by a prefix sum of per-group m-tile counts
 // computed by wave 0 (group g owns tiles [exc*tiles_n, inc*tiles_n)).
 template <int BM, int BN>
-__device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
+__device__ bool resolve_tile(const GemmArgs &p, Tile *t, int block, int nblocks) {
     const int tiles_n = (p.N + BN - 1) / BN;
     if (p.group_mode == GM_KSPLIT) {
         const int tiles_m = (p.M + BM - 1) / BM;
         const int per_g = tiles_m * tiles_n;
-        const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
+        const int bid = xcd_tile_order(block, nblocks);
         const int g = bid / per_g;
         if (g >= p.G) return false;
         const int rem = bid - g * per_g;
@@ -183,7 +188,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t) {
             if (lane >= off) inc += v;
         }
         const int exc = inc - cnt;
-        const int bid = xcd_tile_order(blockIdx.x, gridDim.x);
+        const int bid = xcd_tile_order(block, nblocks);
         const int mt_global = bid / tiles_n;   // past the last group's tiles: no tile
         if (mt_global >= exc && mt_global < inc) {
             int b = exc;
@@ -221,7 +226,7 @@ template <int BM, int BN>
 inline int64_t gemm_grid(const GemmArgs &p) {
     const int64_t tiles_n = (p.N + BN - 1) / BN;
     if (p.group_mode == GM_KSPLIT) return static_cast<int64_t>(p.G) * ((p.M + BM - 1) / BM) * tiles_n;
-    return ((p.extent + BM - 1) / BM + p.G) * tiles_n;
+    return ((p.extent + BM - 1) / BM + p.G) * tiles_n * (p.kparts > 1 ? p.kparts : 1);
 }
 
 // Per-group operand base pointers (element offsets).
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
     __shared__ __align__(16) bf16_t Bs[2][NB][BN * LDK];
 
     Tile t;
-    if (!resolve_tile<BM, BN>(p, &t)) return;
+    if (!resolve_tile<BM, BN>(p, &t, blockIdx.x, gridDim.x)) return;
     const GroupPtrs<bf16_t> q = group_ptrs<bf16_t>(p, t);
     const int m0 = t.mt * BM, n0 = t.nt * BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -793,8 +798,17 @@ void gemm_dma_kernel(GemmArgs p) {
     __shared__ __align__(1024) char smem[S * kStage];
 
     Tile t;
-    if (!resolve_tile<BM, BN>(p, &t)) return;
-    const GroupPtrs<bf16_t> q = group_ptrs<bf16_t>(p, t);
+    // a split over k gives consecutive blocks the parts of one tile
+    const int kparts = p.group_mode == GM_ROWS && p.kparts > 1 ? p.kparts : 1;
+    const int kpart = static_cast<int>(blockIdx.x) % kparts;
+    if (!resolve_tile<BM, BN>(p, &t, blockIdx.x / kparts, gridDim.x / kparts)) return;
+    GroupPtrs<bf16_t> q = group_ptrs<bf16_t>(p, t);
+    int kstart = 0;
+    if (kparts > 1) {
+        kstart = kpart * p.kpart_len;
+        t.Kg = min(t.Kg, kstart + p.kpart_len);
+        q.coff += static_cast<int64_t>(kpart) * p.c_gstride;
+    }
     const int m0 = t.mt * BM, n0 = t.nt * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -802,9 +816,9 @@ void gemm_dma_kernel(GemmArgs p) {
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
     const bool wact = m0 + wm * WTM < t.Mg && n0 + wn * WTN < p.N;  // this wave has output
 
-    const int ktiles = (t.Kg + BK - 1) / BK;
+    const int ktiles = (t.Kg - kstart + BK - 1) / BK;
     const int nph = p.group_mode == GM_KSPLIT ? 1 : p.nphase;
-    const int total = ktiles * nph;
+    const int total = t.Kg > kstart ? ktiles * nph : 0;
 
     PA pa;
     PB pb;
@@ -854,7 +868,7 @@ void gemm_dma_kernel(GemmArgs p) {
         StagePlan sp;
         const bool live = st < total;
         const int ph = (live && st >= ktiles) ? 1 : 0;
-        const int k0 = live ? (st - ph * ktiles) * BK : 0;
+        const int k0 = live ? kstart + (st - ph * ktiles) * BK : 0;
         sp.kc = live ? k0 : INT_MAX;
         sp.kadd = 2 * k0;
         if constexpr (A_KC) sp.ra = ph ? ra1 : ra0;
@@ -1155,7 +1169,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     __shared__ float As[BK][BM];
     __shared__ float Bs[NB][BK][BN];
     Tile t;
-    if (!resolve_tile<BM, BN>(p, &t)) return;
+    if (!resolve_tile<BM, BN>(p, &t, blockIdx.x, gridDim.x)) return;
     const GroupPtrs<float> q = group_ptrs<float>(p, t);
     const int m0 = t.mt * BM, n0 = t.nt * BN;
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;

@@ -20,7 +20,8 @@ struct PftPtrs {
 // router
 hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d, int E, int k, float inv_tau,
                         const float *logit_bias, const float *select_bias, int32_t *topk_ids, float *topk_w,
-                        float *logits, hipStream_t s);
+                        float *logits, void *ws, hipStream_t s);
+size_t route_workspace(int64_t T, int d, int E, int dt);
 size_t route_bwd_workspace(int64_t T, int d, int E, int dt);
 hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
                             const float *dtopk_w, int64_t T, int d, int E, int k, float inv_tau, void *dx,

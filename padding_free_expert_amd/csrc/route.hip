@@ -26,8 +26,13 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// When `part` is set, the logits are first formed from nparts fp32 partial
+// sums of z (a split of the d reduction, summed in part order), then scaled and
+// biased with one IEEE operation each and written to `logits`.
 template <int Q>
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ logits,
+__global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ logits, const float *__restrict__ part,
+                                                           int nparts, int64_t part_stride, float scale,
+                                                           const float *__restrict__ lbias,
                                                            const float *__restrict__ sbias, int64_t T, int E, int k,
                                                            int32_t *__restrict__ ids, float *__restrict__ w) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
@@ -41,7 +46,16 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
         s[q] = -INFINITY;
         sel[q] = -INFINITY;
         if (e < E) {
-            s[q] = logits[t * E + e];
+            if (part) {
+                float z = part[t * E + e];
+                for (int pi = 1; pi < nparts; ++pi) z += part[pi * part_stride + t * E + e];
+                float v = __fmul_rn(z, scale);
+                if (lbias) v = __fadd_rn(v, lbias[e]);
+                logits[t * E + e] = v;
+                s[q] = v;
+            } else {
+                s[q] = logits[t * E + e];
+            }
             sel[q] = sbias ? __fadd_rn(s[q], sbias[e]) : s[q];
             mx = fmaxf(mx, s[q]);
         }
@@ -154,7 +168,7 @@ inline int q_of(int E) {
 inline int rbwd_splits(int64_t T, int d, int E) {
     const int64_t tiles = ((d + 127) / 128) * ((E + 63) / 64);
     int64_t S = (512 + tiles - 1) / tiles;
-    const int64_t maxS = (T + 1023) / 1024;
+    const int64_t maxS = (T + 255) / 256;
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
     if (S > 64) S = 64;
@@ -165,9 +179,27 @@ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255);
 
 }  // namespace
 
+// bf16 logits: the d reduction is split into kparts ranges so that the skinny
+// product (T x d times d x E) still gives the device a few hundred blocks; the
+// partial sums land in the workspace and the top-k kernel adds them in order.
+int route_kparts(int64_t T, int d, int E) {
+    const int64_t tiles = ((T + 127) / 128) * ((E + 63) / 64);
+    int64_t kp = (512 + tiles - 1) / tiles;
+    const int64_t maxkp = d / 256;  // each part at least 256 of d
+    if (kp > maxkp) kp = maxkp;
+    if (kp < 1) kp = 1;
+    if (kp > 16) kp = 16;
+    return static_cast<int>(kp);
+}
+
+size_t route_workspace(int64_t T, int d, int E, int dt) {
+    if (dt != kBF16 || T <= 0) return 0;
+    return static_cast<size_t>(route_kparts(T, d, E)) * static_cast<size_t>(T) * E * 4;
+}
+
 hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d, int E, int k, float inv_tau,
                         const float *logit_bias, const float *select_bias, int32_t *topk_ids, float *topk_w,
-                        float *logits, hipStream_t s) {
+                        float *logits, void *ws, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     GemmArgs p{};
     p.group_mode = GM_ROWS;
@@ -182,21 +214,38 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
     p.lda = d;
     p.B0 = wg;
     p.ldb = E;
-    p.C0 = logits;
     p.ldc = E;
     p.scale = inv_tau;
     p.col_bias = logit_bias;
-    hipError_t err = dt == kBF16 ? launch_gemm_mfma<128, 64, 64, 4, 1, 1, true, false, EPI_ROUTER, float>(p, s)
-                                 : launch_gemm_f32<1, true, false, EPI_ROUTER>(p, s);
+    hipError_t err;
+    float *part = nullptr;
+    int kparts = 1;
+    if (dt == kBF16) {
+        kparts = route_kparts(T, d, E);
+        part = static_cast<float *>(ws);
+        p.C0 = part;
+        p.kparts = kparts;
+        p.kpart_len = ((d / kparts + 31) / 32) * 32;
+        p.c_gstride = T * E;
+        err = launch_gemm_dma<128, 64, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s);
+    } else {
+        p.C0 = logits;
+        err = launch_gemm_f32<1, true, false, EPI_ROUTER>(p, s);
+    }
     if (err != hipSuccess) return err;
     const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves)), block(256);
+    const int64_t ps = T * E;
+#define XMOE_TOPK(Q)                                                                                          \
+    hipLaunchKernelGGL(topk_softmax_kernel<Q>, grid, block, 0, s, logits, part, kparts, ps, inv_tau, logit_bias, \
+                       select_bias, T, E, k, topk_ids, topk_w)
     switch (q_of(E)) {
-        case 1: hipLaunchKernelGGL(topk_softmax_kernel<1>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
-        case 2: hipLaunchKernelGGL(topk_softmax_kernel<2>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
-        case 4: hipLaunchKernelGGL(topk_softmax_kernel<4>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
-        case 8: hipLaunchKernelGGL(topk_softmax_kernel<8>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
-        default: hipLaunchKernelGGL(topk_softmax_kernel<16>, grid, block, 0, s, logits, select_bias, T, E, k, topk_ids, topk_w); break;
+        case 1: XMOE_TOPK(1); break;
+        case 2: XMOE_TOPK(2); break;
+        case 4: XMOE_TOPK(4); break;
+        case 8: XMOE_TOPK(8); break;
+        default: XMOE_TOPK(16); break;
     }
+#undef XMOE_TOPK
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ import torch
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_workspace_size, xmoe_combine, xmoe_combine_bwd,
                xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_expert_ffn_gather,
                xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
-               xmoe_route_bwd_workspace_size)
+               xmoe_route_bwd_workspace_size, xmoe_route_workspace_size)
 
 
 class PaddingFreeMoE:
@@ -56,6 +56,7 @@ class PaddingFreeMoE:
         self.logits = torch.empty((T, E), **f32)
         self.pft = PFT(T, E, k, dev)
         self.pft_ws = torch.empty(max(xmoe_build_pft_workspace_size(T, E, k), 16), dtype=torch.uint8, device=dev)
+        self.route_ws = torch.empty(max(xmoe_route_workspace_size(T, d, E, dt), 16), dtype=torch.uint8, device=dev)
         # scratch of the backward (re-gathered rows), not kept from the forward
         self.xs = torch.empty((R, d), dtype=dt, device=dev) if backward else None
         self.act = torch.empty((R, h), dtype=dt, device=dev)
@@ -114,7 +115,7 @@ class PaddingFreeMoE:
             if side is main:
                 mark("shared_ffn")
         xmoe_route(x, w["wg"], self.k, self.topk_ids, self.topk_w, self.logits, self.inv_tau,
-                   w.get("logit_bias"), w.get("select_bias"), stream=main)
+                   w.get("logit_bias"), w.get("select_bias"), workspace=self.route_ws, stream=main)
         mark("route")
         xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=main)
         mark("build_pft")

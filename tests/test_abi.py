@@ -42,21 +42,25 @@ def test_workspace_queries(xm):
     assert xm.xmoe_build_pft_workspace_size(10, 8, 9) == 0          # k > E
     assert xm.xmoe_build_pft_workspace_size(10, 2000, 2) == 0       # E > 1024
     assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 64, torch.bfloat16) >= 4096 * 64 * 2
+    assert xm.xmoe_route_workspace_size(4096, 2048, 64, torch.bfloat16) >= 4096 * 64 * 4
+    assert xm.xmoe_route_workspace_size(4096, 2048, 64, torch.float32) == 0
     assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 0, torch.bfloat16) == 0
 
 
 def test_invalid_arguments_rejected_on_host(xm):
     lib = xm._lib
     # xmoe_route with NULL pointers
-    assert xm._lib_route(None, None, 1, 10, 8, 8, 2, 1.0, None, None, None, None, None, None) == 1
+    assert xm._lib_route(None, None, 1, 10, 8, 8, 2, 1.0, None, None, None, None, None, None, 0, None) == 1
     assert b"NULL" in xm._lib_last_error()
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails before any use
     # k > E
-    assert xm._lib_route(p, p, 1, 10, 8, 8, 9, 1.0, None, None, p, p, p, None) == 1
+    assert xm._lib_route(p, p, 1, 10, 8, 8, 9, 1.0, None, None, p, p, p, None, 0, None) == 1
     # unknown dtype
-    assert xm._lib_route(p, p, 7, 10, 8, 8, 2, 1.0, None, None, p, p, p, None) == 2
+    assert xm._lib_route(p, p, 7, 10, 8, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 2
     # bf16 with d not a multiple of 8
-    assert xm._lib_route(p, p, 1, 10, 12, 8, 2, 1.0, None, None, p, p, p, None) == 2
+    assert xm._lib_route(p, p, 1, 10, 12, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 2
+    # bf16 routing without its workspace
+    assert xm._lib_route(p, p, 1, 10, 64, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 3
     # expert FFN: h not a multiple of 8, E out of range, NULL offsets
     assert xm._lib_up(p, p, p, 1, p, 4, 100, 64, 12, p, None, None) == 2
     assert xm._lib_up(p, p, p, 1, p, 0, 100, 64, 64, p, None, None) == 1
