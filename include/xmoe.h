@@ -266,6 +266,28 @@ xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, 
                                 void *dw1, void *dw3, void *dw2, void *stream);
 
 /*
+ * The four products of xmoe_expert_ffn_bwd as separate calls, so that a
+ * caller can run the weight gradients on another stream beside the data
+ * gradients (same definitions, arguments, limits and results):
+ *   _dact : dh13 from dye, w2 and the saved h13       (needs nothing else)
+ *   _dx   : dxs from dh13, w1, w3                     (after _dact)
+ *   _dw13 : dw1, dw3 from xs and dh13                 (after _dact)
+ *   _dw2  : dw2 from act and dye                      (independent of the rest)
+ */
+xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void *h13,
+                                     xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                                     int64_t rows, int32_t d, int32_t h, void *dh13, void *stream);
+xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3,
+                                   xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                                   int64_t rows, int32_t d, int32_t h, void *dxs, void *stream);
+xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtype dtype,
+                                     const int32_t *expert_offsets, int32_t E, int64_t rows,
+                                     int32_t d, int32_t h, void *dw1, void *dw3, void *stream);
+xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,
+                                    const int32_t *expert_offsets, int32_t E, int64_t rows,
+                                    int32_t d, int32_t h, void *dw2, void *stream);
+
+/*
  * Backward of the dispatch (the transpose of the gather):
  *   dx[t] = sum_{j=0..k-1} dxs[slot_to_row[t*k+j]]  (+ dx_add[t])
  * summed in fp32 in slot order, rounded once; no atomics.  dx_add [T,d] may be

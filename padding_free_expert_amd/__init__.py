@@ -20,7 +20,8 @@ __all__ = [
     "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
-    "xmoe_expert_ffn_bwd", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
+    "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13",
+    "xmoe_expert_ffn_bwd_dw2", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +73,10 @@ _lib_combine_bwd = _sig("xmoe_combine_bwd", [_vp, _vp, ctypes.POINTER(_CPft), _i
                                              _vp, _vp, _vp])
 _lib_ffn_bwd = _sig("xmoe_expert_ffn_bwd", [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64,
                                             _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp])
+_lib_bwd_dact = _sig("xmoe_expert_ffn_bwd_dact", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+_lib_bwd_dx = _sig("xmoe_expert_ffn_bwd_dx", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+_lib_bwd_dw13 = _sig("xmoe_expert_ffn_bwd_dw13", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp])
+_lib_bwd_dw2 = _sig("xmoe_expert_ffn_bwd_dw2", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
 _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp,
                                                _vp, _vp])
 _lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
@@ -248,6 +253,34 @@ def xmoe_expert_ffn_bwd(xs, w1, w3, w2, act, h13, dye, expert_offsets, dh13, dxs
     _check(_lib_ffn_bwd(_ptr(xs), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(act), _ptr(h13), _ptr(dye), _dt(xs),
                         _ptr(expert_offsets), E, rows, d, h, _ptr(dh13), _ptr(dxs), _ptr(dw1), _ptr(dw3),
                         _ptr(dw2), _stream(stream)), "xmoe_expert_ffn_bwd")
+
+
+def xmoe_expert_ffn_bwd_dact(dye, w2, h13, expert_offsets, dh13, stream=None):
+    rows, d = dye.shape
+    E, h, _ = w2.shape
+    _check(_lib_bwd_dact(_ptr(dye), _ptr(w2), _ptr(h13), _dt(dye), _ptr(expert_offsets), E, rows, d, h, _ptr(dh13),
+                         _stream(stream)), "xmoe_expert_ffn_bwd_dact")
+
+
+def xmoe_expert_ffn_bwd_dx(dh13, w1, w3, expert_offsets, dxs, stream=None):
+    rows, d = dxs.shape
+    E, _, h = w1.shape
+    _check(_lib_bwd_dx(_ptr(dh13), _ptr(w1), _ptr(w3), _dt(dh13), _ptr(expert_offsets), E, rows, d, h, _ptr(dxs),
+                       _stream(stream)), "xmoe_expert_ffn_bwd_dx")
+
+
+def xmoe_expert_ffn_bwd_dw13(xs, dh13, expert_offsets, dw1, dw3, stream=None):
+    rows, d = xs.shape
+    E, _, h = dw1.shape
+    _check(_lib_bwd_dw13(_ptr(xs), _ptr(dh13), _dt(xs), _ptr(expert_offsets), E, rows, d, h, _ptr(dw1), _ptr(dw3),
+                         _stream(stream)), "xmoe_expert_ffn_bwd_dw13")
+
+
+def xmoe_expert_ffn_bwd_dw2(act, dye, expert_offsets, dw2, stream=None):
+    rows, h = act.shape
+    E, _, d = dw2.shape
+    _check(_lib_bwd_dw2(_ptr(act), _ptr(dye), _dt(act), _ptr(expert_offsets), E, rows, d, h, _ptr(dw2),
+                        _stream(stream)), "xmoe_expert_ffn_bwd_dw2")
 
 
 def xmoe_dispatch_bwd(dxs, pft: PFT, T: int, dx, dx_add=None, stream=None):

@@ -328,6 +328,58 @@ xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, 
                       "xmoe_expert_ffn_bwd launch");
 }
 
+xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void *h13, xmoe_dtype dtype,
+                                     const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
+                                     void *dh13, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(w2 && (rows == 0 || (dye && h13 && dh13)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    REQUIRE(aligned16(dye) && aligned16(w2) && aligned16(h13) && aligned16(dh13), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dact(dtype, dye, w2, h13, expert_offsets, E, rows, d, h, dh13, S(stream)),
+                      "xmoe_expert_ffn_bwd_dact launch");
+}
+
+xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3, xmoe_dtype dtype,
+                                   const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
+                                   void *dxs, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(w1 && w3 && (rows == 0 || (dh13 && dxs)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    REQUIRE(aligned16(dh13) && aligned16(w1) && aligned16(w3) && aligned16(dxs), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dx(dtype, dh13, w1, w3, expert_offsets, E, rows, d, h, dxs, S(stream)),
+                      "xmoe_expert_ffn_bwd_dx launch");
+}
+
+xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtype dtype,
+                                     const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
+                                     void *dw1, void *dw3, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(dw1 && dw3 && (rows == 0 || (xs && dh13)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    REQUIRE(aligned16(xs) && aligned16(dh13) && aligned16(dw1) && aligned16(dw3), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, xs, dh13, expert_offsets, E, rows, d, h, dw1, dw3, S(stream)),
+                      "xmoe_expert_ffn_bwd_dw13 launch");
+}
+
+xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,
+                                    const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
+                                    void *dw2, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(dw2 && (rows == 0 || (act && dye)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    REQUIRE(aligned16(act) && aligned16(dye) && aligned16(dw2), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dw2(dtype, act, dye, expert_offsets, E, rows, d, h, dw2, S(stream)),
+                      "xmoe_expert_ffn_bwd_dw2 launch");
+}
+
 xmoe_status xmoe_dispatch_bwd(const void *dxs, const xmoe_pft *pft, int64_t T, int32_t d, int32_t k, xmoe_dtype dtype,
                               const void *dx_add, void *dx, void *stream) {
     TRY(check_dtype(dtype));

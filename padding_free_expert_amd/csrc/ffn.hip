@@ -102,82 +102,106 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
                                        : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
 }
 
-hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
-                          const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d, int h,
-                          void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s) {
+// dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13
+hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const void *h13, const int32_t *offsets, int E,
+                               int64_t rows, int d, int h, void *dh13, hipStream_t s) {
+    const int64_t dh = static_cast<int64_t>(d) * h;
+    hipError_t err;
+    GemmArgs p = rows_args(offsets, E, rows);
+    p.N = h;
+    p.K = d;
+    p.A0 = dye;
+    p.lda = d;
+    p.B0 = w2;          // B(k=c, n=j) = W2[e][j*d + c]
+    p.ldb = d;
+    p.b_gstride = dh;
+    p.C0 = dh13;
+    p.ldc = 2 * static_cast<int64_t>(h);
+    p.aux = h13;
+    p.ld_aux = 2 * static_cast<int64_t>(h);
+    p.hoff = h;
+    err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
+          : large_tiles(rows, E, h, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
+                                         : launch_gemm_dma<128, 128, 64, 2, 2, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
+    return err;
+}
+
+// dxs = dH1 . W1[e]^T + dH3 . W3[e]^T
+hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
+                             int64_t rows, int d, int h, void *dxs, hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     const size_t esz = dt == kBF16 ? 2 : 4;
     hipError_t err;
-    {   // dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13
-        GemmArgs p = rows_args(offsets, E, rows);
-        p.N = h;
-        p.K = d;
-        p.A0 = dye;
-        p.lda = d;
-        p.B0 = w2;          // B(k=c, n=j) = W2[e][j*d + c]
-        p.ldb = d;
-        p.b_gstride = dh;
-        p.C0 = dh13;
-        p.ldc = 2 * static_cast<int64_t>(h);
-        p.aux = h13;
-        p.ld_aux = 2 * static_cast<int64_t>(h);
-        p.hoff = h;
-        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
-              : large_tiles(rows, E, h, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
-                                             : launch_gemm_dma<128, 128, 64, 2, 2, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
-        if (err != hipSuccess) return err;
-    }
-    {   // dxs = dH1 . W1[e]^T + dH3 . W3[e]^T
-        GemmArgs p = rows_args(offsets, E, rows);
-        p.N = d;
-        p.K = h;
-        p.nphase = 2;
-        p.A0 = dh13;
-        p.A1 = static_cast<const char *>(dh13) + h * esz;
-        p.lda = 2 * static_cast<int64_t>(h);
-        p.B0 = w1;          // B(k=j, n=i) = W1[e][i*h + j]
-        p.B1 = w3;
-        p.ldb = h;
-        p.b_gstride = dh;
-        p.C0 = dxs;
-        p.ldc = d;
-        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(p, s)
-              : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
-                                             : launch_gemm_dma<256, 256, 32, 2, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
-        if (err != hipSuccess) return err;
-    }
-    {   // dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert)
-        GemmArgs p = ksplit_args(offsets, E, rows);
-        p.M = d;
-        p.N = h;
-        p.A0 = xs;          // A(m=i, k=r) = xs[r*d + i]
-        p.lda = d;
-        p.B0 = dh13;        // B(k=r, n=j) = dh13[r*2h + j]
-        p.Bx = static_cast<const char *>(dh13) + h * esz;
-        p.ldb = 2 * static_cast<int64_t>(h);
-        p.C0 = dw1;
-        p.Cx = dw3;
-        p.ldc = h;
-        p.c_gstride = dh;
-        err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
-                          : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
-        if (err != hipSuccess) return err;
-    }
-    {   // dW2[e] = act_e^T . dye_e
-        GemmArgs p = ksplit_args(offsets, E, rows);
-        p.M = h;
-        p.N = d;
-        p.A0 = act;         // A(m=j, k=r) = act[r*h + j]
-        p.lda = h;
-        p.B0 = dye;         // B(k=r, n=c) = dye[r*d + c]
-        p.ldb = d;
-        p.C0 = dw2;
-        p.ldc = d;
-        p.c_gstride = dh;
-        err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(p, s)
-              : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, false, false, 4, EPI_STORE, bf16_t, 1>(p, s)
-                                             : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
-    }
+    GemmArgs p = rows_args(offsets, E, rows);
+    p.N = d;
+    p.K = h;
+    p.nphase = 2;
+    p.A0 = dh13;
+    p.A1 = static_cast<const char *>(dh13) + h * esz;
+    p.lda = 2 * static_cast<int64_t>(h);
+    p.B0 = w1;          // B(k=j, n=i) = W1[e][i*h + j]
+    p.B1 = w3;
+    p.ldb = h;
+    p.b_gstride = dh;
+    p.C0 = dxs;
+    p.ldc = d;
+    err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(p, s)
+          : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                         : launch_gemm_dma<256, 256, 32, 2, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
+    return err;
+}
+
+// dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert)
+hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const int32_t *offsets, int E, int64_t rows,
+                               int d, int h, void *dw1, void *dw3, hipStream_t s) {
+    const int64_t dh = static_cast<int64_t>(d) * h;
+    const size_t esz = dt == kBF16 ? 2 : 4;
+    hipError_t err;
+    GemmArgs p = ksplit_args(offsets, E, rows);
+    p.M = d;
+    p.N = h;
+    p.A0 = xs;          // A(m=i, k=r) = xs[r*d + i]
+    p.lda = d;
+    p.B0 = dh13;        // B(k=r, n=j) = dh13[r*2h + j]
+    p.Bx = static_cast<const char *>(dh13) + h * esz;
+    p.ldb = 2 * static_cast<int64_t>(h);
+    p.C0 = dw1;
+    p.Cx = dw3;
+    p.ldc = h;
+    p.c_gstride = dh;
+    err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
+                      : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
+    return err;
+}
+
+// dW2[e] = act_e^T . dye_e
+hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const int32_t *offsets, int E, int64_t rows,
+                              int d, int h, void *dw2, hipStream_t s) {
+    const int64_t dh = static_cast<int64_t>(d) * h;
+    hipError_t err;
+    GemmArgs p = ksplit_args(offsets, E, rows);
+    p.M = h;
+    p.N = d;
+    p.A0 = act;         // A(m=j, k=r) = act[r*h + j]
+    p.lda = h;
+    p.B0 = dye;         // B(k=r, n=c) = dye[r*d + c]
+    p.ldb = d;
+    p.C0 = dw2;
+    p.ldc = d;
+    p.c_gstride = dh;
+    err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(p, s)
+          : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, false, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                         : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
+    return err;
+}
+
+hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
+                          const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d, int h,
+                          void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s) {
+    hipError_t err = launch_ffn_bwd_dact(dt, dye, w2, h13, offsets, E, rows, d, h, dh13, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dx(dt, dh13, w1, w3, offsets, E, rows, d, h, dxs, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dw13(dt, xs, dh13, offsets, E, rows, d, h, dw1, dw3, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dw2(dt, act, dye, offsets, E, rows, d, h, dw2, s);
     return err;
 }
 

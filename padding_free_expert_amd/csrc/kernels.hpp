@@ -48,6 +48,15 @@ hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t
                          void *h13, hipStream_t s);
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows,
                            int d, int h, void *ye, hipStream_t s);
+// the four products of the expert backward, each on its own stream if the caller wants
+hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const void *h13, const int32_t *offsets, int E,
+                               int64_t rows, int d, int h, void *dh13, hipStream_t s);
+hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
+                             int64_t rows, int d, int h, void *dxs, hipStream_t s);
+hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const int32_t *offsets, int E, int64_t rows,
+                               int d, int h, void *dw1, void *dw3, hipStream_t s);
+hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const int32_t *offsets, int E, int64_t rows,
+                              int d, int h, void *dw2, hipStream_t s);
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
                           const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d,
                           int h, void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s);

@@ -13,7 +13,8 @@ from typing import Dict, Optional
 import torch
 
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_workspace_size, xmoe_combine, xmoe_combine_bwd,
-               xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_expert_ffn_gather,
+               xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd, xmoe_expert_ffn_bwd_dact,
+               xmoe_expert_ffn_bwd_dw13, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx, xmoe_expert_ffn_gather,
                xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
                xmoe_route_bwd_workspace_size, xmoe_route_workspace_size)
 
@@ -46,8 +47,10 @@ class PaddingFreeMoE:
         self.lean = lean
         # the shared experts depend only on x (forward) and dy (backward): with
         # overlap they run on a second stream (default priority) beside the
-        # routed path and fill the tail of its GEMMs
+        # routed path and fill the tail of its GEMMs; the routed weight
+        # gradients run on a third one beside the data gradients
         self.overlap = overlap
+        self.wside = torch.cuda.Stream(device=self.device) if backward else None
         dev, dt = self.device, self.dtype
         T, d, E, h, R = T, self.d, self.E, self.h, T * k
         f32 = dict(dtype=torch.float32, device=dev)
@@ -155,12 +158,25 @@ class PaddingFreeMoE:
             xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, w["w1"], w["w3"], self.pft.expert_offsets,
                                       self.act, self.h13, stream=main)
             mark("recompute_h13")
-        xmoe_dispatch(self.x, self.k, self.pft, self.xs, stream=main)
-        mark("dispatch")
-        xmoe_expert_ffn_bwd(self.xs, w["w1"], w["w3"], w["w2"], self.act, self.h13, self.dye,
-                            self.pft.expert_offsets, self.dh13, self.dxs, self.dw1, self.dw3, self.dw2,
-                            stream=main)
-        mark("expert_ffn_bwd")
+        off = self.pft.expert_offsets
+        ws = self.wside if self.overlap else main
+        # weight gradients: dW2 needs act and dye only; dW1/dW3 need the rows
+        # (re-gathered as scratch) and dH1/dH3
+        ws.wait_stream(main)
+        xmoe_expert_ffn_bwd_dw2(self.act, self.dye, off, self.dw2, stream=ws)
+        if ws is main:
+            mark("bwd_dw2")
+        xmoe_dispatch(self.x, self.k, self.pft, self.xs, stream=ws)
+        if ws is main:
+            mark("dispatch")
+        xmoe_expert_ffn_bwd_dact(self.dye, w["w2"], self.h13, off, self.dh13, stream=main)
+        mark("bwd_dact")
+        ws.wait_stream(main)
+        xmoe_expert_ffn_bwd_dw13(self.xs, self.dh13, off, self.dw1, self.dw3, stream=ws)
+        if ws is main:
+            mark("bwd_dw13")
+        xmoe_expert_ffn_bwd_dx(self.dh13, w["w1"], w["w3"], off, self.dxs, stream=main)
+        mark("bwd_dx")
         if self.shared:
             main.wait_stream(side)
         xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=main)
@@ -168,6 +184,7 @@ class PaddingFreeMoE:
         xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.dx, self.dwg,
                        self.rbwd_ws, self.inv_tau, stream=main)
         mark("route_bwd")
+        main.wait_stream(self.wside)  # every gradient is complete in the caller's stream order
         return self.dx
 
     def saved_bytes(self) -> int:

@@ -227,6 +227,33 @@ def test_expert_ffn_forward(xm, dtype, rows, d, h, E, empty):
     assert_close(host(ye), ref["ye"], rt, "ye")
 
 
+def test_expert_ffn_bwd_split_calls_match_composite(xm):
+    """The four backward products called one by one (as a caller running the
+    weight gradients on another stream does) give bitwise the composite call's
+    results."""
+    dtype, rows, d, h, E, empty = "bf16", 517, 328, 264, 7, 0.3
+    off, xs, w1, w3, w2, _ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=11)
+    c = lambda t: t.cuda()
+    tdt = DT[dtype]
+    act = torch.empty((rows, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((rows, 2 * h), dtype=tdt, device="cuda")
+    ye = torch.empty((rows, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn(c(xs), c(w1), c(w3), c(w2), c(off), act, ye, h13=h13)
+    dye = c(workloads.random_rows(rows, d, dtype, seed=12))
+    bufs = lambda: (torch.empty((rows, 2 * h), dtype=tdt, device="cuda"), torch.empty((rows, d), dtype=tdt, device="cuda"),
+                    torch.empty((E, d, h), dtype=tdt, device="cuda"), torch.empty((E, d, h), dtype=tdt, device="cuda"),
+                    torch.empty((E, h, d), dtype=tdt, device="cuda"))
+    a = bufs()
+    xm.xmoe_expert_ffn_bwd(c(xs), c(w1), c(w3), c(w2), act, h13, dye, c(off), *a)
+    b = bufs()
+    xm.xmoe_expert_ffn_bwd_dw2(act, dye, c(off), b[4])
+    xm.xmoe_expert_ffn_bwd_dact(dye, c(w2), h13, c(off), b[0])
+    xm.xmoe_expert_ffn_bwd_dw13(c(xs), b[0], c(off), b[2], b[3])
+    xm.xmoe_expert_ffn_bwd_dx(b[0], c(w1), c(w3), c(off), b[1])
+    for name, u, v in zip(["dh13", "dxs", "dw1", "dw3", "dw2"], a, b):
+        assert torch.equal(u, v), name
+
+
 GATHER_CASES = [
     ("f32", 97, 64, 40, 5, 2, 0.0),
     ("bf16", 300, 256, 200, 16, 6, 1.5),   # skewed: some experts empty
