@@ -122,7 +122,7 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
     p.hoff = h;
     err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
           : large_tiles(rows, E, h, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
-                                         : launch_gemm_dma<128, 128, 64, 2, 2, 1, true, true, 2, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
+                                         : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
     return err;
 }
 
