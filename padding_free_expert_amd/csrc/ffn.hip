@@ -169,8 +169,12 @@ hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const i
     p.Cx = dw3;
     p.ldc = h;
     p.c_gstride = dh;
-    err = dt == kBF16 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s)
-                      : launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
+    // short reductions (few rows per expert) leave each tile little work to
+    // hide its pipeline fill and epilogue behind: three blocks per compute unit
+    // (two-slot rings) overlap more of them
+    if (dt != kBF16) return launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
+    err = rows / (E > 0 ? E : 1) < 1024 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 2, EPI_STORE, bf16_t, 3>(p, s)
+                                        : launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
     return err;
 }
 

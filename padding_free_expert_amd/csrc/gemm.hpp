@@ -788,7 +788,7 @@ void gemm_dma_kernel(GemmArgs p) {
     constexpr int kStage = kABytes + NB * kBBytes;
     constexpr int kL = PA::kN + NB * PB::kN;   // loads per thread per k block
     static_assert(S >= 2 && kL * (S - 2) <= 63, "vmcnt range");
-    static_assert(OCC == 1 || S * kStage <= 80 * 1024 - 64, "two blocks per CU need at most 80 KiB of LDS each");
+    static_assert(S * kStage <= 160 * 1024 / OCC - 64, "OCC blocks per CU must fit the 160 KiB of LDS");
     constexpr int KK = BK / 16;
     static_assert(KK == 2 || KK == 4, "BK must be 32 or 64");
     constexpr int NM = NB * TN * TM;                 // products per k step
