@@ -169,7 +169,7 @@ xmoe_status xmoe_dispatch(const void *x, xmoe_dtype dtype, int64_t T, int32_t d,
  * offsets[E] == rows (segments are clamped to [0, rows]).  The launch is sized
  * on the host from `rows` and E alone; the tile scheduler reads the offsets on
  * the device, so nothing is copied back.  Empty experts cost nothing.
- * Limits: d, h multiples of 8; E <= 1024; rows < 2^31.
+ * Limits: d, h multiples of 8 and at most 2^20; E <= 1024; rows < 2^31.
  */
 xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, xmoe_dtype dtype,
                                const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d,

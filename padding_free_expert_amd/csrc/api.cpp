@@ -103,6 +103,8 @@ xmoe_status check_ffn_sizes(const int32_t *offsets, int32_t E, int64_t rows, int
     REQUIRE(rows >= 0 && rows <= kMaxRows, XMOE_ERR_INVALID_VALUE, "rows must be in [0, 2^31)");
     REQUIRE(d >= 1 && h >= 1, XMOE_ERR_INVALID_VALUE, "d and h must be >= 1");
     REQUIRE(d % 8 == 0 && h % 8 == 0, XMOE_ERR_UNSUPPORTED, "d and h must be multiples of 8");
+    // tiles address up to 256 rows of [H1|H3] or of d columns with 32-bit offsets
+    REQUIRE(d <= (1 << 20) && h <= (1 << 20), XMOE_ERR_UNSUPPORTED, "d and h must be at most 2^20");
     return XMOE_OK;
 }
 

@@ -20,6 +20,8 @@
 //   dgrad1   dxs = dH1.W1^T + dH3.W3^T          two k phases, B read k-contiguous
 //   wgrad13  dW1 = xs^T dH1, dW3 = xs^T dH3     reduction over the expert's rows
 //   wgrad2   dW2 = act^T dye                    reduction over the expert's rows
+#include <cmath>
+
 #include "common.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
@@ -40,13 +42,30 @@ GemmArgs rows_args(const int32_t *offsets, int E, int64_t rows) {
 
 // Large tiles (256-row, eight waves) cut the bytes each product moves from L2
 // into LDS by a third, but they round every expert's rows up to a multiple of
-// 256 and need enough tiles to fill the device.  They are used when the
-// average group has at least 1024 rows and the large-tile grid still gives two
-// blocks per compute unit; otherwise the 128-row, two-blocks-per-CU tiles.
+// 256 and need enough tiles to fill the device (the grid must still give two
+// blocks per compute unit).  large_tiles: the average group has at least 1024
+// rows, where the rounding costs little.
+bool large_grid(int64_t rows, int E, int64_t n, int bn) {
+    return (rows / 256 + E) * ((n + bn - 1) / bn) >= 512;
+}
 bool large_tiles(int64_t rows, int E, int64_t n, int bn) {
+    return rows / (E > 0 ? E : 1) >= 1024 && large_grid(rows, E, n, bn);
+}
+// The down-projection and dA products also gain from them below 1024 rows when
+// an expert's last 256-row tile is well filled: the mean count's remainder r
+// modulo 256 is at least 96, and two standard deviations of the per-expert
+// count (about sqrt(mean) for uniform routing) above it still stay within the
+// tile, so few experts spill into an almost empty extra tile.  Measured small
+// against large on one device (mean rows 256 .. 1024 per expert): the large
+// tile is 3-14% faster at 384 and 448 rows, level at 640 and 1024, and 5-16%
+// slower at 256, 320, 512 and 768.
+bool large_tiles_filled(int64_t rows, int E, int64_t n, int bn) {
     const int64_t per_group = rows / (E > 0 ? E : 1);
-    const int64_t tiles = (rows / 256 + E) * ((n + bn - 1) / bn);
-    return per_group >= 1024 && tiles >= 512;
+    if (!large_grid(rows, E, n, bn)) return false;
+    if (per_group >= 1024) return true;
+    const int64_t r = per_group % 256;
+    const double sd = std::sqrt(static_cast<double>(per_group));
+    return per_group >= 256 && r >= 96 && static_cast<double>(r) + 2.0 * sd <= 256.0;
 }
 
 GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
@@ -98,8 +117,9 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
     p.C0 = ye;
     p.ldc = d;
     if (dt != kBF16) return launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
-    return large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
-                                       : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
+    return large_tiles_filled(rows, E, d, 256)
+               ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+               : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
 }
 
 // dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13
@@ -121,7 +141,8 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
     p.ld_aux = 2 * static_cast<int64_t>(h);
     p.hoff = h;
     err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
-          : large_tiles(rows, E, h, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
+          : large_tiles_filled(rows, E, h, 256)
+              ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
                                          : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
     return err;
 }
@@ -145,9 +166,10 @@ hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const voi
     p.b_gstride = dh;
     p.C0 = dxs;
     p.ldc = d;
+    // one 256x256 tile of eight waves per compute unit at every size (measured
+    // level with or ahead of four waves from 256 to 1638 rows per expert)
     err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(p, s)
-          : large_tiles(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s)
-                                         : launch_gemm_dma<256, 256, 32, 2, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
+                      : launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
     return err;
 }
 

@@ -1059,44 +1059,60 @@ void gemm_dma_kernel(GemmArgs p) {
         return;
     }
     if constexpr (std::is_same<OutT, bf16_t>::value && EPI == EPI_SWIGLU_BWD) {
-        // Staged SwiGLU backward: the saved H1 and H3 tiles come into the ring
-        // with 16-byte row reads, each lane turns its dA values and the H1/H3 at
-        // the same places into dH1/dH3 in place, and both tiles leave in
-        // 16-byte row chunks.
-        constexpr int LDC = BN + 8;
-        constexpr int kPass = 2 * BM * LDC * 2 <= S * kStage ? 1 : WGM;
-        constexpr int RP = BM / kPass;
-        static_assert(2 * RP * LDC * 2 <= S * kStage, "H1/H3 tiles must fit the ring");
+        // Staged SwiGLU backward, one pass of rows at a time: the saved H1 and
+        // H3 tiles of the pass come into the (now idle) ring by LDS DMA with
+        // every load of the pass in flight at once, each lane turns its dA
+        // values and the H1/H3 at the same places into dH1/dH3 in place, and
+        // both tiles leave in 16-byte row chunks.  Rows are unpadded; 16-byte
+        // chunk c of tile row r sits at chunk c ^ (r % 16), which keeps the
+        // lanes' 8-byte reads (32 rows, one column) and the row reads free of
+        // bank conflicts.
+        constexpr int kRowB = BN * 2;
+        constexpr int kCpr = BN / 8;
+        static_assert(kCpr >= 16 && (kCpr & (kCpr - 1)) == 0, "the chunk swizzle needs 16, 32, ... chunks a row");
+        // wave rows per pass: all of them if both tiles fit the ring, else half, else one
+        constexpr int WPP = 2 * BM * kRowB <= S * kStage                       ? WGM
+                            : (WGM % 2 == 0 && BM * kRowB <= S * kStage)       ? WGM / 2
+                                                                               : 1;
+        constexpr int kPass = WGM / WPP, RP = WPP * WTM;
+        static_assert(2 * RP * kRowB <= S * kStage, "H1/H3 tiles of a pass must fit the ring");
+        constexpr int kBlk = RP * kRowB / 1024;  // 1 KiB loads per tile and pass
+        static_assert(kBlk % NW == 0, "whole loads per wave");
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
         typedef float f4_t __attribute__((ext_vector_type(4)));
-        __bf16 *c1 = reinterpret_cast<__bf16 *>(smem), *c3 = c1 + RP * LDC;
-        const __bf16 *aux = static_cast<const __bf16 *>(p.aux) + q.crow * p.ld_aux;
+        char *const t1 = smem, *const t3 = smem + RP * kRowB;
+        // the saved rows of this tile; rows past the group's end read as zeros
+        const __amdgpu_buffer_rsrc_t raux =
+            make_rsrc(static_cast<const bf16_t *>(p.aux) + (q.crow + m0) * p.ld_aux,
+                      static_cast<int64_t>(t.Mg - m0) * p.ld_aux * 2);
         __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.crow * p.ldc;
         __syncthreads();  // every wave is done with the ring
         for (int pass = 0; pass < kPass; ++pass) {
-#pragma unroll 4
-            for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
-                const int row = c / (BN / 8), c8 = c % (BN / 8);
-                const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
-                if (m < t.Mg && n < p.N) {
-                    *reinterpret_cast<uint4 *>(c1 + row * LDC + 8 * c8) =
-                        *reinterpret_cast<const uint4 *>(aux + m * p.ld_aux + n);
-                    *reinterpret_cast<uint4 *>(c3 + row * LDC + 8 * c8) =
-                        *reinterpret_cast<const uint4 *>(aux + m * p.ld_aux + p.hoff + n);
-                }
+#pragma unroll
+            for (int x = 0; x < kBlk / NW; ++x) {
+                const int blk = x * NW + wave;
+                const int o = blk * 1024 + lane * 16;
+                const int row = o / kRowB, c = ((o % kRowB) / 16) ^ (row & 15);
+                const int col = n0 + 8 * c;
+                const int off = static_cast<int>(((pass * RP + row) * p.ld_aux + col) * 2);
+                const bool ok = col < p.N;
+                lds_dma16(raux, ok ? off : kOob, sbase + blk * 1024);
+                lds_dma16(raux, ok ? off + static_cast<int>(p.hoff * 2) : kOob, sbase + RP * kRowB + blk * 1024);
             }
+            wait_vmem<0>();
             __syncthreads();
-            if (kPass == 1 || wm == pass) {
+            if (wm / WPP == pass) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const int row = (kPass == 1 ? wm * WTM : 0) + i * 32 + (lane & 31);
+                            const int row = (wm % WPP) * WTM + i * 32 + (lane & 31);
                             const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                            bf4_t *p1 = reinterpret_cast<bf4_t *>(c1 + row * LDC + col);
-                            bf4_t *p3 = reinterpret_cast<bf4_t *>(c3 + row * LDC + col);
+                            const int at = row * kRowB + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7);
+                            bf4_t *p1 = reinterpret_cast<bf4_t *>(t1 + at);
+                            bf4_t *p3 = reinterpret_cast<bf4_t *>(t3 + at);
                             const f4_t h1 = __builtin_convertvector(*p1, f4_t), h3 = __builtin_convertvector(*p3, f4_t);
                             f4_t g1, g3;
 #pragma unroll
@@ -1112,14 +1128,14 @@ void gemm_dma_kernel(GemmArgs p) {
             }
             __syncthreads();
 #pragma unroll 4
-            for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
-                const int row = c / (BN / 8), c8 = c % (BN / 8);
+            for (int c = threadIdx.x; c < RP * kCpr; c += NT) {
+                const int row = c / kCpr, c8 = c % kCpr;
                 const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
                 if (m < t.Mg && n < p.N) {
-                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) =
-                        *reinterpret_cast<const uint4 *>(c1 + row * LDC + 8 * c8);
+                    const int at = row * kRowB + 16 * (c8 ^ (row & 15));
+                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) = *reinterpret_cast<const uint4 *>(t1 + at);
                     *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
-                        *reinterpret_cast<const uint4 *>(c3 + row * LDC + 8 * c8);
+                        *reinterpret_cast<const uint4 *>(t3 + at);
                 }
             }
             if (pass + 1 < kPass) __syncthreads();
