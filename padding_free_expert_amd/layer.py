@@ -153,6 +153,15 @@ class PaddingFreeMoE:
             dx_add = self.sh_dx
         xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w, stream=main)
         mark("combine_bwd")
+        if self.shared:
+            # the gate's backward needs only dtopk_w, the logits and x: it runs
+            # beside the expert backward and adds dz . wg^T into the shared
+            # experts' dx, which the dispatch backward folds into dx
+            side.wait_stream(main)
+            xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.sh_dx, self.dwg,
+                           self.rbwd_ws, self.inv_tau, stream=side)
+            if side is main:
+                mark("route_bwd")
         if self.lean:
             # recompute the pre-activations (act is rewritten with the same values)
             xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, w["w1"], w["w3"], self.pft.expert_offsets,
@@ -181,9 +190,10 @@ class PaddingFreeMoE:
             main.wait_stream(side)
         xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=main)
         mark("dispatch_bwd")
-        xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.dx, self.dwg,
-                       self.rbwd_ws, self.inv_tau, stream=main)
-        mark("route_bwd")
+        if not self.shared:
+            xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, self.dx, self.dwg,
+                           self.rbwd_ws, self.inv_tau, stream=main)
+            mark("route_bwd")
         main.wait_stream(self.wside)  # every gradient is complete in the caller's stream order
         return self.dx
 
