@@ -316,6 +316,80 @@ xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits,
                            int64_t T, int32_t d, int32_t E, int32_t k, float inv_temperature,
                            void *dx, float *dwg, void *workspace, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Pilot tokens of Redundancy-Bypassing Dispatch, stage 1
+ * (X-MoE article, adg.csdn.net, section 2.2.1 "分层冗余消除算法", Pilot Token选择):
+ *   node(e) = e / experts_per_node;   pilots = {(t, node(topk_ids[t,j]))}
+ * i.e. a token's k destinations deduplicated per node.  Listed by node, then
+ * token (the Padding-Free Token buffer's order with the node as the key).
+ * Outputs (DEVICE, int32, caller-owned; N = E / experts_per_node,
+ * P = node_offsets[N] <= T * min(k, N)):
+ *   pilot_token_ids [>= P], pilot_node_ids [>= P]   -- pilot p carries token
+ *       pilot_token_ids[p] to node pilot_node_ids[p];
+ *   node_counts [N], node_offsets [N+1]             -- node n's pilots are
+ *       [node_offsets[n], node_offsets[n+1]);
+ *   slot_to_pilot [T*k]                            -- the pilot that carries
+ *       slot (t, j) to its expert's node.
+ * Sizing pilot_token_ids / pilot_node_ids for T*k rows is always enough.
+ * topk_ids: DEVICE int32 [T,k]; ids outside [0, E) are skipped (their slot
+ * gets -1).  experts_per_node must divide E; E <= 1024.  workspace: device,
+ * 16-byte aligned, >= xmoe_build_pilots_workspace_size.  No host sync.
+ */
+size_t xmoe_build_pilots_workspace_size(int64_t T, int32_t E, int32_t k, int32_t experts_per_node);
+xmoe_status xmoe_build_pilots(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k, int32_t experts_per_node,
+                              int32_t *pilot_token_ids, int32_t *pilot_node_ids, int32_t *node_counts,
+                              int32_t *node_offsets, int32_t *slot_to_pilot, void *workspace, size_t ws_bytes,
+                              void *stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-parallel plans ("5.4 MoE模型在分布式训练中的应用", section 专家并行:
+ * 数据流, All-to-All通信步骤; the X-MoE article, section 2.1.1, sends the
+ * Padding-Free Token rows with an alltoallv and no padding).  G ranks; rank q
+ * holds the E/G consecutive experts [q*E/G, (q+1)*E/G).  This library plans
+ * and rearranges; the exchange itself (RCCL alltoallv of the counts, then of
+ * the rows) is the caller's.
+ *
+ * xmoe_ep_send_plan: from a rank's Padding-Free Token buffer, the rows it sends
+ * to each rank -- one contiguous run each, since the buffer is expert-sorted:
+ *   send_counts[q] = expert_offsets[(q+1)E/G] - expert_offsets[qE/G]   [G]
+ *   send_displs[q] = expert_offsets[qE/G]                              [G+1]
+ * (DEVICE int32, caller-owned).  G must divide E; E <= 1024.
+ */
+xmoe_status xmoe_ep_send_plan(const int32_t *expert_offsets, int32_t E, int32_t G, int32_t *send_counts,
+                              int32_t *send_displs, void *stream);
+
+/*
+ * xmoe_ep_recv_plan: the receiver's layout.  recv_counts: DEVICE int32
+ * [G, E_local], row s = the tokens_per_expert source s sends for this rank's
+ * E_local experts.  Rows arrive source-major (source s, its experts ascending,
+ * its row order) and are regrouped expert-major (local expert e, then source
+ * s, then the same order), which the grouped expert GEMMs read:
+ *   local_offsets [E_local+1]  expert e's rows in the expert-major layout;
+ *   recv_displs   [G+1]        source s's rows in the arrival layout;
+ *   local_to_recv [n_recv]     arrival index of expert-major row m;
+ *   recv_to_local [n_recv]     its inverse.
+ * n_recv (host) must equal the sum of recv_counts (the caller knows it: the
+ * alltoallv needs it); rows past n_recv are never written, so a wrong n_recv
+ * gives a wrong but memory-safe plan.  G * E_local <= 1024.  workspace: device,
+ * 16-byte aligned, >= xmoe_ep_recv_plan_workspace_size.
+ * Regroup with xmoe_scatter_rows(recv, ..., recv_to_local, ...) and send the
+ * expert outputs back with xmoe_scatter_rows(out, ..., local_to_recv, ...).
+ */
+size_t xmoe_ep_recv_plan_workspace_size(int32_t G, int32_t E_local);
+xmoe_status xmoe_ep_recv_plan(const int32_t *recv_counts, int32_t G, int32_t E_local, int64_t n_recv,
+                              int32_t *local_offsets, int32_t *recv_displs, int32_t *local_to_recv,
+                              int32_t *recv_to_local, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Row scatter: dst[index[i], :] = src[i, :] for i < n; index values outside
+ * [0, dst_rows) are skipped.  src [n, d], dst [dst_rows, d], row-major, DEVICE,
+ * 16-byte aligned; index DEVICE int32 [n].  d a multiple of 8.  With a
+ * permutation index this is the EP regroup (and, with the inverse, the
+ * ungroup).  Overlapping src and dst are not allowed.
+ */
+xmoe_status xmoe_scatter_rows(const void *src, xmoe_dtype dtype, int64_t n, int32_t d, const int32_t *index,
+                              int64_t dst_rows, void *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

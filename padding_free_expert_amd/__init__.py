@@ -22,6 +22,8 @@ __all__ = [
     "xmoe_combine", "xmoe_combine_bwd",
     "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13",
     "xmoe_expert_ffn_bwd_dw2", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
+    "xmoe_build_pilots_workspace_size", "xmoe_build_pilots", "xmoe_ep_send_plan", "xmoe_ep_recv_plan_workspace_size",
+    "xmoe_ep_recv_plan", "xmoe_scatter_rows",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +84,12 @@ _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64,
 _lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
 _lib_rbwd = _sig("xmoe_route_bwd", [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp,
                                     _vp, _vp, _sz, _vp])
+_lib_pilots_ws = _sig("xmoe_build_pilots_workspace_size", [_i64, _i32, _i32, _i32], _sz)
+_lib_pilots = _sig("xmoe_build_pilots", [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_lib_ep_send = _sig("xmoe_ep_send_plan", [_vp, _i32, _i32, _vp, _vp, _vp])
+_lib_ep_recv_ws = _sig("xmoe_ep_recv_plan_workspace_size", [_i32, _i32], _sz)
+_lib_ep_recv = _sig("xmoe_ep_recv_plan", [_vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_lib_scatter_rows = _sig("xmoe_scatter_rows", [_vp, ctypes.c_int, _i64, _i32, _vp, _i64, _vp, _vp])
 
 
 class XmoeError(RuntimeError):
@@ -302,3 +310,43 @@ def xmoe_route_bwd(x, wg, logits, topk_ids, dtopk_w, dx, dwg, workspace, inv_tem
     _check(_lib_rbwd(_ptr(x), _ptr(wg), _ptr(logits), _ptr(topk_ids), _ptr(dtopk_w), _dt(x), T, d, E, k,
                      inv_temperature, _ptr(dx), _ptr(dwg), _ptr(workspace),
                      workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_route_bwd")
+
+
+def xmoe_build_pilots_workspace_size(T: int, E: int, k: int, experts_per_node: int) -> int:
+    return int(_lib_pilots_ws(T, E, k, experts_per_node))
+
+
+def xmoe_build_pilots(topk_ids, E: int, experts_per_node: int, pilot_token_ids, pilot_node_ids, node_counts,
+                      node_offsets, slot_to_pilot, workspace, stream=None):
+    """Pilot tokens of Redundancy-Bypassing Dispatch (see xmoe.h); all int32 device tensors."""
+    T, k = topk_ids.shape
+    _check(_lib_pilots(_ptr(topk_ids), T, E, k, experts_per_node, _ptr(pilot_token_ids), _ptr(pilot_node_ids),
+                       _ptr(node_counts), _ptr(node_offsets), _ptr(slot_to_pilot), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_build_pilots")
+
+
+def xmoe_ep_send_plan(expert_offsets, G: int, send_counts, send_displs, stream=None):
+    E = expert_offsets.numel() - 1
+    _check(_lib_ep_send(_ptr(expert_offsets), E, G, _ptr(send_counts), _ptr(send_displs), _stream(stream)),
+           "xmoe_ep_send_plan")
+
+
+def xmoe_ep_recv_plan_workspace_size(G: int, E_local: int) -> int:
+    return int(_lib_ep_recv_ws(G, E_local))
+
+
+def xmoe_ep_recv_plan(recv_counts, n_recv: int, local_offsets, recv_displs, local_to_recv, recv_to_local,
+                      workspace, stream=None):
+    """recv_counts: int32 device [G, E_local]; n_recv: its sum (host int)."""
+    G, el = recv_counts.shape
+    _check(_lib_ep_recv(_ptr(recv_counts), G, el, n_recv, _ptr(local_offsets), _ptr(recv_displs),
+                        _ptr(local_to_recv), _ptr(recv_to_local), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_ep_recv_plan")
+
+
+def xmoe_scatter_rows(src, index, dst, n: Optional[int] = None, stream=None):
+    """dst[index[i]] = src[i] for i < n (default: all rows of src)."""
+    rows, d = src.shape
+    n = rows if n is None else n
+    _check(_lib_scatter_rows(_ptr(src), _dt(src), n, d, _ptr(index), dst.shape[0], _ptr(dst), _stream(stream)),
+           "xmoe_scatter_rows")

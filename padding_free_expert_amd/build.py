@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libxmoe.so")
-SOURCES = ["api.cpp", "route.hip", "pft.hip", "rows.hip", "ffn.hip"]
+SOURCES = ["api.cpp", "route.hip", "pft.hip", "rows.hip", "ffn.hip", "ep.hip"]
 
 
 def _hipcc() -> str:

@@ -424,4 +424,84 @@ xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits, c
                       "xmoe_route_bwd launch");
 }
 
+/* ---------------------------------------------- pilot tokens and EP plans */
+
+size_t xmoe_build_pilots_workspace_size(int64_t T, int32_t E, int32_t k, int32_t experts_per_node) {
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || T * static_cast<int64_t>(k) > kMaxRows ||
+        experts_per_node < 1 || E % experts_per_node != 0)
+        return 0;
+    return xmoe::pft_workspace(T, E / experts_per_node);
+}
+
+xmoe_status xmoe_build_pilots(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k, int32_t experts_per_node,
+                              int32_t *pilot_token_ids, int32_t *pilot_node_ids, int32_t *node_counts,
+                              int32_t *node_offsets, int32_t *slot_to_pilot, void *workspace, size_t ws_bytes,
+                              void *stream) {
+    REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
+    REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
+    REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
+    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    REQUIRE(experts_per_node >= 1 && E % experts_per_node == 0, XMOE_ERR_INVALID_VALUE,
+            "experts_per_node must divide E");
+    REQUIRE(node_counts && node_offsets, XMOE_ERR_INVALID_VALUE, "node_counts and node_offsets are required");
+    REQUIRE(T == 0 || (topk_ids && pilot_token_ids && pilot_node_ids && slot_to_pilot), XMOE_ERR_INVALID_VALUE,
+            "topk_ids, pilot_token_ids, pilot_node_ids and slot_to_pilot are required");
+    const size_t need = xmoe::pft_workspace(T, E / experts_per_node);
+    REQUIRE(workspace && aligned16(workspace), XMOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+    REQUIRE(ws_bytes >= need, XMOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+    CHECK_DEVICE();
+    const xmoe::PilotPtrs pl{pilot_token_ids, pilot_node_ids, node_counts, node_offsets, slot_to_pilot};
+    return hip_status(xmoe::launch_build_pilots(topk_ids, T, E, k, experts_per_node, pl, workspace, S(stream)),
+                      "xmoe_build_pilots launch");
+}
+
+xmoe_status xmoe_ep_send_plan(const int32_t *expert_offsets, int32_t E, int32_t G, int32_t *send_counts,
+                              int32_t *send_displs, void *stream) {
+    REQUIRE(expert_offsets && send_counts && send_displs, XMOE_ERR_INVALID_VALUE,
+            "expert_offsets, send_counts and send_displs are required");
+    REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
+    REQUIRE(G >= 1 && E % G == 0, XMOE_ERR_INVALID_VALUE, "G must divide E");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ep_send_plan(expert_offsets, E, G, send_counts, send_displs, S(stream)),
+                      "xmoe_ep_send_plan launch");
+}
+
+size_t xmoe_ep_recv_plan_workspace_size(int32_t G, int32_t E_local) {
+    if (G < 1 || E_local < 1 || static_cast<int64_t>(G) * E_local > 1024) return 0;
+    return xmoe::ep_recv_plan_workspace(G, E_local);
+}
+
+xmoe_status xmoe_ep_recv_plan(const int32_t *recv_counts, int32_t G, int32_t E_local, int64_t n_recv,
+                              int32_t *local_offsets, int32_t *recv_displs, int32_t *local_to_recv,
+                              int32_t *recv_to_local, void *workspace, size_t ws_bytes, void *stream) {
+    REQUIRE(recv_counts && local_offsets && recv_displs, XMOE_ERR_INVALID_VALUE,
+            "recv_counts, local_offsets and recv_displs are required");
+    REQUIRE(G >= 1 && E_local >= 1 && static_cast<int64_t>(G) * E_local <= 1024, XMOE_ERR_INVALID_VALUE,
+            "G >= 1, E_local >= 1 and G*E_local <= 1024 are required");
+    REQUIRE(n_recv >= 0 && n_recv <= kMaxRows, XMOE_ERR_INVALID_VALUE, "n_recv must be in [0, 2^31)");
+    REQUIRE(n_recv == 0 || (local_to_recv && recv_to_local), XMOE_ERR_INVALID_VALUE,
+            "local_to_recv and recv_to_local are required");
+    const size_t need = xmoe::ep_recv_plan_workspace(G, E_local);
+    REQUIRE(workspace && aligned16(workspace), XMOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+    REQUIRE(ws_bytes >= need, XMOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ep_recv_plan(recv_counts, G, E_local, n_recv, local_offsets, recv_displs,
+                                                local_to_recv, recv_to_local, workspace, S(stream)),
+                      "xmoe_ep_recv_plan launch");
+}
+
+xmoe_status xmoe_scatter_rows(const void *src, xmoe_dtype dtype, int64_t n, int32_t d, const int32_t *index,
+                              int64_t dst_rows, void *dst, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(n >= 0 && n <= kMaxRows && dst_rows >= 0 && dst_rows <= kMaxRows, XMOE_ERR_INVALID_VALUE,
+            "n and dst_rows must be in [0, 2^31)");
+    REQUIRE(n == 0 || (src && index && dst), XMOE_ERR_INVALID_VALUE, "src, index and dst are required");
+    REQUIRE(d >= 1, XMOE_ERR_INVALID_VALUE, "d must be >= 1");
+    REQUIRE(d % 8 == 0, XMOE_ERR_UNSUPPORTED, "d must be a multiple of 8");
+    REQUIRE(aligned16(src) && aligned16(dst), XMOE_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_scatter_rows(dtype, src, n, d, index, dst_rows, dst, S(stream)),
+                      "xmoe_scatter_rows launch");
+}
+
 }  // extern "C"

@@ -32,9 +32,27 @@ size_t pft_workspace(int64_t T, int E);
 hipError_t launch_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k,
                             const PftPtrs &pft, void *ws, hipStream_t s);
 
+// pilot tokens (Redundancy-Bypassing Dispatch, stage 1); workspace pft_workspace(T, E / experts_per_node)
+struct PilotPtrs {
+    int32_t *pilot_token_ids, *pilot_node_ids, *node_counts, *node_offsets, *slot_to_pilot;
+};
+hipError_t launch_build_pilots(const int32_t *topk_ids, int64_t T, int E, int k, int experts_per_node,
+                               const PilotPtrs &pl, void *ws, hipStream_t s);
+
+// expert-parallel plans
+hipError_t launch_ep_send_plan(const int32_t *expert_offsets, int E, int G, int32_t *send_counts,
+                               int32_t *send_displs, hipStream_t s);
+size_t ep_recv_plan_workspace(int G, int el);
+hipError_t launch_ep_recv_plan(const int32_t *recv_counts, int G, int el, int64_t n, int32_t *local_offsets,
+                               int32_t *recv_displs, int32_t *local_to_recv, int32_t *recv_to_local, void *ws,
+                               hipStream_t s);
+
 // row movement
 hipError_t launch_dispatch(int dt, const void *x, const int32_t *slot_to_row, int64_t T, int d, int k, void *xs,
                            hipStream_t s);
+// dst[index[i]] = src[i] for i < n (indices outside [0, dst_rows) skipped)
+hipError_t launch_scatter_rows(int dt, const void *src, int64_t n, int d, const int32_t *index, int64_t dst_rows,
+                               void *dst, hipStream_t s);
 hipError_t launch_gather_sum(int dt, const void *src, const int32_t *slot_to_row, const float *weights, int64_t T,
                              int d, int k, const void *add, void *out, hipStream_t s);
 hipError_t launch_combine_bwd(int dt, const void *dy, const void *ye, const int32_t *slot_to_row,

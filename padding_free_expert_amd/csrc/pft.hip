@@ -17,6 +17,14 @@
 //   3. scatter: each block rebuilds its bitmap; the row of (t, e) is the
 //               block's base for e plus the number of lower tokens of the block
 //               whose bit for e is set -- a stable (expert, token) order.
+//
+// The same kernels build the pilot tokens of Redundancy-Bypassing Dispatch
+// (X-MoE article, section 2.2.1 "分层冗余消除算法", Pilot Token选择): the key
+// of a slot is then its expert's node, e / experts_per_node, and the bitmap
+// keeps one bit per (node, token) however many of the token's experts sit on
+// that node -- the per-node deduplication -- so the rows are the (token, node)
+// pilots, listed by node, then token, and every slot of a token bound for one
+// node gets the same pilot row.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,8 +36,12 @@ constexpr int kChunk = 256;          // tokens per block
 constexpr int kWords = kChunk / 32;  // bitmap words per expert
 constexpr int kMaxE = 1024;
 
-__device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int64_t T, int E, int k) {
-    for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) bm[i] = 0u;
+// key of an expert id: e / div (div = 1: the expert; experts per node: the node)
+__device__ __forceinline__ int key_of(int e, int div) { return div == 1 ? e : e / div; }
+
+__device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int64_t T, int E, int k, int div) {
+    const int nk = E / div;
+    for (int i = threadIdx.x; i < nk * kWords; i += blockDim.x) bm[i] = 0u;
     __syncthreads();
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
     if (t < T) {
@@ -37,21 +49,22 @@ __device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int6
         const int w = threadIdx.x >> 5;
         for (int j = 0; j < k; ++j) {
             const int e = ids[t * k + j];
-            if (e >= 0 && e < E) atomicOr(&bm[e * kWords + w], bit);
+            if (e >= 0 && e < E) atomicOr(&bm[key_of(e, div) * kWords + w], bit);
         }
     }
     __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
-                                                        int32_t *__restrict__ counts) {
+                                                        int div, int32_t *__restrict__ counts) {
     __shared__ uint32_t bm[kMaxE * kWords];
-    build_bitmap(bm, ids, T, E, k);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    build_bitmap(bm, ids, T, E, k, div);
+    const int nk = E / div;
+    for (int e = threadIdx.x; e < nk; e += blockDim.x) {
         int c = 0;
 #pragma unroll
         for (int w = 0; w < kWords; ++w) c += __popc(bm[e * kWords + w]);
-        counts[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+        counts[static_cast<int64_t>(blockIdx.x) * nk + e] = c;
     }
 }
 
@@ -91,29 +104,32 @@ __global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restric
 
 __global__ __launch_bounds__(256) void pft_scatter_kernel(const int32_t *__restrict__ ids,
                                                           const float *__restrict__ wt, int64_t T, int E, int k,
-                                                          const int32_t *__restrict__ base, int32_t *__restrict__ tok,
-                                                          int32_t *__restrict__ eid, float *__restrict__ cw,
-                                                          int32_t *__restrict__ s2r) {
+                                                          int div, const int32_t *__restrict__ base,
+                                                          int32_t *__restrict__ tok, int32_t *__restrict__ eid,
+                                                          float *__restrict__ cw, int32_t *__restrict__ s2r) {
     __shared__ uint32_t bm[kMaxE * kWords];
-    build_bitmap(bm, ids, T, E, k);
+    build_bitmap(bm, ids, T, E, k, div);
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
     if (t >= T) return;
     const int64_t R = T * k;
+    const int nk = E / div;
     const int wd = threadIdx.x >> 5;
     const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
     for (int j = 0; j < k; ++j) {
         const int e = ids[t * k + j];
         int64_t r = -1;
+        int key = -1;
         if (e >= 0 && e < E) {
-            int rank = __popc(bm[e * kWords + wd] & below);
-            for (int q = 0; q < wd; ++q) rank += __popc(bm[e * kWords + q]);
-            r = base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+            key = key_of(e, div);
+            int rank = __popc(bm[key * kWords + wd] & below);
+            for (int q = 0; q < wd; ++q) rank += __popc(bm[key * kWords + q]);
+            r = base[static_cast<int64_t>(blockIdx.x) * nk + key] + rank;
             if (r >= R) r = -1;
         }
         s2r[t * k + j] = static_cast<int32_t>(r);
-        if (r >= 0) {
+        if (r >= 0) {  // a token's slots bound for one key write the same row with the same values
             if (tok) tok[r] = static_cast<int32_t>(t);
-            if (eid) eid[r] = e;
+            if (eid) eid[r] = key;
             if (cw) cw[r] = wt ? wt[t * k + j] : 0.0f;
         }
     }
@@ -126,23 +142,42 @@ size_t pft_workspace(int64_t T, int E) {
     return static_cast<size_t>(2 * nblk * E) * sizeof(int32_t) + 256;
 }
 
-hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, const PftPtrs &pft, void *ws,
-                            hipStream_t s) {
+namespace {
+
+// Stable counting sort of the slots by key (expert, or node when div > 1).
+hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int k, int div, int32_t *tok, int32_t *keyid,
+                      int32_t *count_per_key, int32_t *offsets, float *cw, int32_t *s2r, void *ws, hipStream_t s) {
     const int64_t nblk = (T + kChunk - 1) / kChunk;
+    const int nk = E / div;
     int32_t *counts = static_cast<int32_t *>(ws);
-    int32_t *base = counts + nblk * E;
+    int32_t *base = counts + nblk * nk;
     if (nblk > 0) {
-        hipLaunchKernelGGL(pft_count_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, counts);
+        hipLaunchKernelGGL(pft_count_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, div,
+                           counts);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(pft_scan_kernel, dim3(1), dim3(1024), 0, s, counts, static_cast<int>(nblk), E, base,
-                       pft.tokens_per_expert, pft.expert_offsets);
+    hipLaunchKernelGGL(pft_scan_kernel, dim3(1), dim3(1024), 0, s, counts, static_cast<int>(nblk), nk, base,
+                       count_per_key, offsets);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
-    hipLaunchKernelGGL(pft_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, base,
-                       pft.token_ids, pft.expert_ids, pft.combine_weights, pft.slot_to_row);
+    hipLaunchKernelGGL(pft_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, div,
+                       base, tok, keyid, cw, s2r);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, const PftPtrs &pft, void *ws,
+                            hipStream_t s) {
+    return keyed_sort(ids, w, T, E, k, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
+                      pft.combine_weights, pft.slot_to_row, ws, s);
+}
+
+hipError_t launch_build_pilots(const int32_t *ids, int64_t T, int E, int k, int experts_per_node,
+                               const PilotPtrs &pl, void *ws, hipStream_t s) {
+    return keyed_sort(ids, nullptr, T, E, k, experts_per_node, pl.pilot_token_ids, pl.pilot_node_ids, pl.node_counts,
+                      pl.node_offsets, nullptr, pl.slot_to_pilot, ws, s);
 }
 
 }  // namespace xmoe

@@ -175,6 +175,19 @@ hipError_t launch_dispatch(int dt, const void *x, const int32_t *s2r, int64_t T,
     return hipGetLastError();
 }
 
+// One row per source index: the dispatch copy with one destination per row.
+hipError_t launch_scatter_rows(int dt, const void *src, int64_t n, int d, const int32_t *index, int64_t dst_rows,
+                               void *dst, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (dt == kBF16)
+        hipLaunchKernelGGL(dispatch_kernel<bf16_t>, dim3(token_blocks(n)), dim3(256), 0, s,
+                           static_cast<const bf16_t *>(src), index, n, d, 1, dst_rows, static_cast<bf16_t *>(dst));
+    else
+        hipLaunchKernelGGL(dispatch_kernel<float>, dim3(token_blocks(n)), dim3(256), 0, s,
+                           static_cast<const float *>(src), index, n, d, 1, dst_rows, static_cast<float *>(dst));
+    return hipGetLastError();
+}
+
 hipError_t launch_gather_sum(int dt, const void *src, const int32_t *s2r, const float *weights, int64_t T, int d,
                              int k, const void *add, void *out, hipStream_t s) {
     if (T <= 0) return hipSuccess;

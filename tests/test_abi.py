@@ -71,3 +71,22 @@ def test_invalid_arguments_rejected_on_host(xm):
     # dispatch: T*k overflow
     assert lib.xmoe_dispatch(p, 1, ctypes.c_int64(1 << 30), 64, 8, ctypes.byref(pft), p, None) == 1
     assert xm._lib_last_error() != b""
+
+
+def test_pilot_and_ep_entry_points_reject_on_host(xm):
+    p = ctypes.c_void_p(16)  # never dereferenced
+    assert xm.xmoe_build_pilots_workspace_size(4096, 64, 6, 8) >= 16 * 8 * 4
+    assert xm.xmoe_build_pilots_workspace_size(4096, 64, 6, 5) == 0      # 5 does not divide 64
+    assert xm.xmoe_ep_recv_plan_workspace_size(8, 8) >= 2 * 64 * 4
+    assert xm.xmoe_ep_recv_plan_workspace_size(64, 32) == 0              # more than 1024 cells
+    # pilots: experts_per_node not dividing E; workspace too small
+    assert xm._lib_pilots(p, 100, 64, 6, 5, p, p, p, p, p, p, 1 << 20, None) == 1
+    assert xm._lib_pilots(p, 100000, 64, 6, 8, p, p, p, p, p, p, 16, None) == 3
+    # send plan: G not dividing E
+    assert xm._lib_ep_send(p, 64, 6, p, p, None) == 1
+    # recv plan: too many cells, missing maps
+    assert xm._lib_ep_recv(p, 64, 32, 10, p, p, p, p, p, 1 << 20, None) == 1
+    assert xm._lib_ep_recv(p, 8, 8, 10, p, p, None, p, p, 1 << 20, None) == 1
+    # row scatter: d not a multiple of 8, unknown dtype
+    assert xm._lib_scatter_rows(p, 1, 10, 12, p, 10, p, None) == 2
+    assert xm._lib_scatter_rows(p, 9, 10, 16, p, 10, p, None) == 2
