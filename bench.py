@@ -207,9 +207,65 @@ def main():
            "breakdown_ms_serial": {k: round(v, 4) for k, v in breakdown.items()},
            "roofline": roofline}
 
+    out["ep_rbd"] = ep_rbd(xm, wl, layer, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
+
+
+def ep_rbd(xm, wl, layer, stream, nodes=8, ranks=8, n_rep=20):
+    """Time the expert-parallel plans and the pilot-token build at this shape:
+    pilots of the layer's own routing over `nodes` nodes; the send plan of its
+    buffer over `ranks` ranks; the receive plan and regroup of rank 0 fed by
+    `ranks` sources with independent routings of the same shape."""
+    import torch
+    import workloads
+
+    T, E, k, d = wl.T, wl.E, wl.k, wl.d
+    if E % nodes or E % ranks:
+        return None
+    i32 = dict(dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_rep):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_rep * 1e3  # us
+
+    ids = layer.topk_ids
+    pl = [torch.empty((T * k,), **i32) for _ in range(3)]
+    nc, no = torch.empty((nodes,), **i32), torch.empty((nodes + 1,), **i32)
+    pws = torch.empty(max(xm.xmoe_build_pilots_workspace_size(T, E, k, E // nodes), 16), dtype=torch.uint8,
+                      device="cuda")
+    t_pil = timed(lambda: xm.xmoe_build_pilots(ids, E, E // nodes, pl[0], pl[1], nc, no, pl[2], pws))
+    n_pilots = int(no[-1].item())
+
+    sc, sd = torch.empty((ranks,), **i32), torch.empty((ranks + 1,), **i32)
+    t_send = timed(lambda: xm.xmoe_ep_send_plan(layer.pft.expert_offsets, ranks, sc, sd))
+
+    el = E // ranks
+    C = torch.stack([torch.bincount(workloads.random_topk(T, E, k, seed=100 + s)[0].reshape(-1).long(),
+                                    minlength=E)[:el] for s in range(ranks)]).to(torch.int32)
+    n = int(C.sum())
+    Cd = C.cuda()
+    lo, rd = torch.empty((el + 1,), **i32), torch.empty((ranks + 1,), **i32)
+    l2r, r2l = torch.empty((n,), **i32), torch.empty((n,), **i32)
+    rws = torch.empty(max(xm.xmoe_ep_recv_plan_workspace_size(ranks, el), 16), dtype=torch.uint8, device="cuda")
+    t_recv = timed(lambda: xm.xmoe_ep_recv_plan(Cd, n, lo, rd, l2r, r2l, rws))
+    rows = torch.randn(n, d, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(rows)
+    t_reg = timed(lambda: xm.xmoe_scatter_rows(rows, r2l, dst))
+    moved = 2.0 * n * d * 2 + 4.0 * n  # rows read and written once, plus the index
+    return {"pilots": {"nodes": nodes, "experts_per_node": E // nodes, "us": round(t_pil, 2),
+                       "pilots": n_pilots, "slots": T * k, "pilot_fraction": round(n_pilots / (T * k), 4)},
+            "send_plan": {"ranks": ranks, "us": round(t_send, 2)},
+            "recv_plan": {"ranks": ranks, "rows": n, "us": round(t_recv, 2)},
+            "regroup": {"rows": n, "d": d, "us": round(t_reg, 2), "GB_per_s": round(moved / (t_reg * 1e-6) / 1e9, 1)}}
 
 
 def cpu_baseline(wl, inp, sample_tokens):

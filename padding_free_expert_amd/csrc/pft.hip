@@ -55,6 +55,9 @@ __device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int6
     __syncthreads();
 }
 
+// BY_NODE (a compile-time copy of the same code) only names the pilot build's
+// launches apart from the buffer build's in a profile.
+template <bool BY_NODE>
 __global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
                                                         int div, int32_t *__restrict__ counts) {
     __shared__ uint32_t bm[kMaxE * kWords];
@@ -69,6 +72,7 @@ __global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restric
 }
 
 // One block of 1024 threads; thread e owns expert e.
+template <bool BY_NODE>
 __global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restrict__ counts, int nblk, int E,
                                                         int32_t *__restrict__ base, int32_t *__restrict__ tpe,
                                                         int32_t *__restrict__ offsets) {
@@ -102,6 +106,7 @@ __global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restric
     }
 }
 
+template <bool BY_NODE>
 __global__ __launch_bounds__(256) void pft_scatter_kernel(const int32_t *__restrict__ ids,
                                                           const float *__restrict__ wt, int64_t T, int E, int k,
                                                           int div, const int32_t *__restrict__ base,
@@ -145,6 +150,7 @@ size_t pft_workspace(int64_t T, int E) {
 namespace {
 
 // Stable counting sort of the slots by key (expert, or node when div > 1).
+template <bool BY_NODE>
 hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int k, int div, int32_t *tok, int32_t *keyid,
                       int32_t *count_per_key, int32_t *offsets, float *cw, int32_t *s2r, void *ws, hipStream_t s) {
     const int64_t nblk = (T + kChunk - 1) / kChunk;
@@ -152,16 +158,16 @@ hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int 
     int32_t *counts = static_cast<int32_t *>(ws);
     int32_t *base = counts + nblk * nk;
     if (nblk > 0) {
-        hipLaunchKernelGGL(pft_count_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, div,
+        hipLaunchKernelGGL(pft_count_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, div,
                            counts);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(pft_scan_kernel, dim3(1), dim3(1024), 0, s, counts, static_cast<int>(nblk), nk, base,
+    hipLaunchKernelGGL(pft_scan_kernel<BY_NODE>, dim3(1), dim3(1024), 0, s, counts, static_cast<int>(nblk), nk, base,
                        count_per_key, offsets);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
-    hipLaunchKernelGGL(pft_scatter_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, div,
+    hipLaunchKernelGGL(pft_scatter_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, div,
                        base, tok, keyid, cw, s2r);
     return hipGetLastError();
 }
@@ -170,13 +176,13 @@ hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int 
 
 hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, const PftPtrs &pft, void *ws,
                             hipStream_t s) {
-    return keyed_sort(ids, w, T, E, k, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
+    return keyed_sort<false>(ids, w, T, E, k, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
                       pft.combine_weights, pft.slot_to_row, ws, s);
 }
 
 hipError_t launch_build_pilots(const int32_t *ids, int64_t T, int E, int k, int experts_per_node,
                                const PilotPtrs &pl, void *ws, hipStream_t s) {
-    return keyed_sort(ids, nullptr, T, E, k, experts_per_node, pl.pilot_token_ids, pl.pilot_node_ids, pl.node_counts,
+    return keyed_sort<true>(ids, nullptr, T, E, k, experts_per_node, pl.pilot_token_ids, pl.pilot_node_ids, pl.node_counts,
                       pl.node_offsets, nullptr, pl.slot_to_pilot, ws, s);
 }
 
