@@ -18,6 +18,14 @@ namespace {
 constexpr int kWaves = 4;      // tokens per 256-thread block
 constexpr int kUnroll = 4;     // 16-byte vectors in flight per lane
 
+// 16-byte store marked non-temporal.  Measured per kernel in the layer: it
+// speeds up the dispatch copy (35 -> 26 us at the DeepSeek-MoE-16B shape) and
+// the gather-sums, and slows the combine backward, which keeps plain stores.
+__device__ __forceinline__ void nt_store16(uint4 v, uint4 *p) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void dispatch_kernel(const T *__restrict__ x, const int32_t *__restrict__ s2r,
                                                        int64_t ntok, int d, int k, int64_t R, T *__restrict__ xs) {
@@ -44,7 +52,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const T *__restrict__ x, 
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int c = c0 + 64 * u;
-                    if (c < nvec) dst[c] = v[u];
+                    if (c < nvec) nt_store16(v[u], &dst[c]);
                 }
             }
         }
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const T *__restrict__ s
 #pragma unroll
                     for (int e = 0; e < V; ++e) acc[u][e] += f[e];
                 }
-                reinterpret_cast<uint4 *>(out + t * d)[c] = Elem<T>::pack(acc[u]);
+                nt_store16(Elem<T>::pack(acc[u]), &reinterpret_cast<uint4 *>(out + t * d)[c]);
             }
         }
     }
