@@ -262,11 +262,10 @@ __device__ __forceinline__ GroupPtrs<T> group_ptrs(const GemmArgs &p, const Tile
     return q;
 }
 
-// ------------------------------------------------------ bf16 matrix-core path
+// ------------------------------------------------------- bf16 helpers
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 // The operands' tile edges (rows past a group's end, k past K) are expressed
@@ -278,119 +277,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
                                              static_cast<int>(n), 0x00020000);
 }
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// 8x8 transpose of 16-bit elements held as 8 rows of 16 bytes: out[j] gets
-// element j of every input row (input row i -> 16-bit lane i of out[j]).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-    uint32_t w[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        w[i][0] = in[i].x; w[i][1] = in[i].y; w[i][2] = in[i].z; w[i][3] = in[i].w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(w[2 * q + 1][j >> 1], w[2 * q][j >> 1], sel);
-        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
-// Global -> register staging of one operand tile of R (m or n) x BK (k)
-// elements, then register -> LDS in the k-contiguous [R][BK+8] layout
-// (the 16-byte row padding spreads both the 16-byte operand reads and the
-// transposed writes over all LDS banks).  Threads [TB, TB+NT) take part.
-template <int R, int BK, bool KC, int TB, int NT>
-struct TileLoader;
-
-// K-contiguous operand: element (r, k) at byte 2*(r*ld + k) from the group base.
-template <int R, int BK, int TB, int NT>
-struct TileLoader<R, BK, true, TB, NT> {
-    static constexpr int kChunks = R * BK / 8;
-    static constexpr int kIter = (kChunks + NT - 1) / NT;
-    uint4 v[kIter];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t r0, int64_t rmax, int64_t k0,
-                                         int64_t kmax) {
-        const int t = static_cast<int>(threadIdx.x) - TB;
-        if (t < 0 || t >= NT) return;
-#pragma unroll
-        for (int i = 0; i < kIter; ++i) {
-            const int c = t + NT * i;
-            const int r = c / (BK / 8), kc = c % (BK / 8);
-            const int64_t gr = r0 + r, gk = k0 + kc * 8;
-            const bool ok = (kChunks % NT == 0 || c < kChunks) && gr < rmax && gk < kmax;
-            v[i] = buf_load16(rs, ok ? static_cast<int>((gr * ld + gk) * 2) : kOob);
-        }
-    }
-    __device__ __forceinline__ void store(bf16_t *lds) const {
-        const int t = static_cast<int>(threadIdx.x) - TB;
-        if (t < 0 || t >= NT) return;
-#pragma unroll
-        for (int i = 0; i < kIter; ++i) {
-            const int c = t + NT * i;
-            if (kChunks % NT == 0 || c < kChunks) {
-                const int r = c / (BK / 8), kc = c % (BK / 8);
-                *reinterpret_cast<uint4 *>(lds + r * (BK + 8) + kc * 8) = v[i];
-            }
-        }
-    }
-};
-
-// MN-contiguous operand: element (r, k) at byte 2*(k*ld + r); moved as 8x8
-// blocks, k-block fastest across lanes so that the transposed LDS writes of a
-// wave land on distinct banks.
-template <int R, int BK, int TB, int NT>
-struct TileLoader<R, BK, false, TB, NT> {
-    static constexpr int kBlocks = (R / 8) * (BK / 8);
-    static constexpr int kIter = (kBlocks + NT - 1) / NT;
-    uint4 v[kIter][8];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t r0, int64_t rmax, int64_t k0,
-                                         int64_t kmax) {
-        const int t = static_cast<int>(threadIdx.x) - TB;
-        if (t < 0 || t >= NT) return;
-#pragma unroll
-        for (int i = 0; i < kIter; ++i) {
-            const int b = t + NT * i;
-            const int kb = b % (BK / 8), rb = b / (BK / 8);
-            const int64_t gr = r0 + rb * 8;
-            const bool ok = (kBlocks % NT == 0 || b < kBlocks) && gr < rmax;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int64_t gk = k0 + kb * 8 + q;
-                v[i][q] = buf_load16(rs, ok && gk < kmax ? static_cast<int>((gk * ld + gr) * 2) : kOob);
-            }
-        }
-    }
-    __device__ __forceinline__ void store(bf16_t *lds) const {
-        const int t = static_cast<int>(threadIdx.x) - TB;
-        if (t < 0 || t >= NT) return;
-#pragma unroll
-        for (int i = 0; i < kIter; ++i) {
-            const int b = t + NT * i;
-            if (kBlocks % NT == 0 || b < kBlocks) {
-                const int kb = b % (BK / 8), rb = b / (BK / 8);
-                uint4 o[8];
-                transpose8x8(v[i], o);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<uint4 *>(lds + (rb * 8 + j) * (BK + 8) + kb * 8) = o[j];
-            }
-        }
-    }
-};
-
-// Thread ranges of the loaders: with two B matrices each takes its own half of
-// the block when its tile is small enough, so no thread does double duty.
-template <int R, int BK, bool KC>
-struct LoaderSplit {
-    static constexpr int kUnits = KC ? R * BK / 8 : (R / 8) * (BK / 8);
-};
 
 // Epilogue on 4 consecutive output columns n..n+3 of row m (all in range).
 template <int EPI, typename OutT>
@@ -470,159 +356,6 @@ __device__ __forceinline__ void epilogue4(const GemmArgs &p, int64_t crow, int64
             *reinterpret_cast<bf4 *>(C0 + row * p.ldc + p.hoff + n) = pack(g3);
         }
     }
-}
-
-// BM x BN tile per 256-thread block (4 waves as WGM x WGN), BK-deep k steps,
-// double-buffered LDS, v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  The
-// B fragment is the instruction's first operand, so each lane accumulates 4
-// consecutive output columns of one output row (vector stores).  NB = 2
-// multiplies the same A tile by two B matrices (W1 and W3 of the
-// up-projection, or dH1 and dH3 of the weight gradient).
-template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int EPI, typename OutT>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs p) {
-    static_assert(WGM * WGN == 4, "four waves per block");
-    constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be a multiple of 32");
-    constexpr int LDK = BK + 8;
-    __shared__ __align__(16) bf16_t As[2][BM * LDK];
-    __shared__ __align__(16) bf16_t Bs[2][NB][BN * LDK];
-
-    Tile t;
-    if (!resolve_tile<BM, BN>(p, &t, blockIdx.x, gridDim.x)) return;
-    const GroupPtrs<bf16_t> q = group_ptrs<bf16_t>(p, t);
-    const int m0 = t.mt * BM, n0 = t.nt * BN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
-
-    f32x16_t acc[NB][TM][TN];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
-
-    const int ktiles = (t.Kg + BK - 1) / BK;
-    const int nph = (p.group_mode == GM_ROWS) ? p.nphase : 1;
-    const int total = ktiles * nph;
-
-    // loader thread ranges: with two B matrices whose tiles need at most half
-    // the block, each gets its own half
-    constexpr int kBUnits = LoaderSplit<BN, BK, B_KC>::kUnits;
-    constexpr bool kSplitB = NB == 2 && kBUnits <= 128;
-    constexpr int kBT0 = 0, kBN0 = kSplitB ? 128 : 256;
-    constexpr int kBT1 = kSplitB ? 128 : 0, kBN1 = kSplitB ? 128 : 256;
-    constexpr int kAUnits = LoaderSplit<BM, BK, A_KC>::kUnits;
-    constexpr int kAT = (kSplitB && kAUnits <= 128) ? 128 : 0;  // A on the half that holds B1
-    constexpr int kAN = (kSplitB && kAUnits <= 128) ? 128 : 256;
-    TileLoader<BM, BK, A_KC, kAT, kAN> la;
-    TileLoader<BN, BK, B_KC, kBT0, kBN0> lb0;
-    TileLoader<BN, BK, B_KC, kBT1, kBN1> lb1;
-
-    // Buffer resources start at the tile's origin, so every offset is small:
-    //  - a k-contiguous operand is based at its first row of the tile;
-    //  - an mn-contiguous operand of the per-group products (the expert
-    //    weights, at most K*N elements) is based at the group;
-    //  - an mn-contiguous operand whose rows are the reduction (GM_KSPLIT) is
-    //    based at the k tile.
-    const bool ksplit = p.group_mode == GM_KSPLIT;
-    auto rsrc_of = [&](const bf16_t *base, bool kc, int r0, int rows_total, int64_t ld, int k0, int64_t &rr0,
-                       int64_t &rmax, int64_t &kk0, int64_t &kmax) {
-        if (kc) {           // rows r0.., k absolute
-            rr0 = 0; rmax = rows_total - r0; kk0 = k0; kmax = t.Kg;
-            return make_rsrc(base + static_cast<int64_t>(r0) * ld, rmax * ld * 2);
-        }
-        if (ksplit) {       // k rows k0.., mn absolute
-            rr0 = r0; rmax = rows_total; kk0 = 0; kmax = t.Kg - k0;
-            return make_rsrc(base + static_cast<int64_t>(k0) * ld, kmax * ld * 2);
-        }
-        rr0 = r0; rmax = rows_total; kk0 = k0; kmax = t.Kg;   // whole [K][N] group operand
-        return make_rsrc(base, static_cast<int64_t>(t.Kg) * ld * 2);
-    };
-    auto load_stage = [&](int it) {
-        const int ph = it >= ktiles ? 1 : 0;
-        const int k0 = (it - ph * ktiles) * BK;
-        int64_t r0, rmax, kk0, kmax;
-        __amdgpu_buffer_rsrc_t rs = rsrc_of(ph ? q.A1 : q.A0, A_KC, m0, t.Mg, p.lda, k0, r0, rmax, kk0, kmax);
-        la.load(rs, p.lda, r0, rmax, kk0, kmax);
-        rs = rsrc_of(ph ? q.B1 : q.B0, B_KC, n0, p.N, p.ldb, k0, r0, rmax, kk0, kmax);
-        lb0.load(rs, p.ldb, r0, rmax, kk0, kmax);
-        if constexpr (NB == 2) {
-            rs = rsrc_of(q.Bx, B_KC, n0, p.N, p.ldb, k0, r0, rmax, kk0, kmax);
-            lb1.load(rs, p.ldb, r0, rmax, kk0, kmax);
-        }
-    };
-    auto store_stage = [&](int buf) {
-        la.store(As[buf]);
-        lb0.store(Bs[buf][0]);
-        if constexpr (NB == 2) lb1.store(Bs[buf][NB - 1]);
-    };
-
-    if (total > 0) {
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-    }
-    for (int it = 0; it < total; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < total) load_stage(it + 1);
-        const bf16_t *as = As[buf] + (wm * WTM + (lane & 31)) * LDK + (lane >> 5) * 8;
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8_t af[TM];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8_t *>(as + i * 32 * LDK + kk);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const bf16_t *bs = Bs[buf][b] + (wn * WTN + (lane & 31)) * LDK + (lane >> 5) * 8;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const bf16x8_t bf = *reinterpret_cast<const bf16x8_t *>(bs + j * 32 * LDK + kk);
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[b][i][j], 0, 0, 0);
-                }
-            }
-        }
-        if (it + 1 < total) store_stage(buf ^ 1);
-        __syncthreads();
-    }
-
-    // accumulator (i, j, r) of lane l holds C[row, col] with
-    //   row = i*32 + l%32,  col = j*32 + 8*(r/4) + 4*(l/32) + r%4
-    const int m_lane = m0 + wm * WTM + (lane & 31);
-    const int n_lane = n0 + wn * WTN + 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m_lane + i * 32;
-        if (m >= t.Mg) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n_lane + j * 32 + 8 * g;
-                if (n >= p.N) continue;
-                float v0[4], v1[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v0[r] = acc[0][i][j][4 * g + r];
-                    v1[r] = acc[NB - 1][i][j][4 * g + r];
-                }
-                epilogue4<EPI, OutT>(p, q.crow, q.coff, m, n, v0, v1);
-            }
-    }
-}
-
-template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int EPI, typename OutT>
-inline hipError_t launch_gemm_mfma(const GemmArgs &p, hipStream_t stream) {
-    const int64_t grid = gemm_grid<BM, BN>(p);
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WGM, WGN, NB, A_KC, B_KC, EPI, OutT>), dim3(static_cast<unsigned>(grid)),
-                       dim3(256), 0, stream, p);
-    return hipGetLastError();
 }
 
 // ------------------------------------------- bf16 pipelined path (LDS DMA)
@@ -1058,34 +791,39 @@ void gemm_dma_kernel(GemmArgs p) {
         }
         return;
     }
-    if constexpr (std::is_same<OutT, bf16_t>::value && EPI == EPI_SWIGLU_BWD) {
-        // Staged SwiGLU backward, one pass of rows at a time: the saved H1 and
-        // H3 tiles of the pass come into the (now idle) ring by LDS DMA with
-        // every load of the pass in flight at once, each lane turns its dA
-        // values and the H1/H3 at the same places into dH1/dH3 in place, and
-        // both tiles leave in 16-byte row chunks.  Rows are unpadded; 16-byte
-        // chunk c of tile row r sits at chunk c ^ (r % 16), which keeps the
-        // lanes' 8-byte reads (32 rows, one column) and the row reads free of
-        // bank conflicts.
+    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_SWIGLU_BWD || EPI == EPI_ACCUM)) {
+        // Staged read-modify-write epilogue, one pass of rows at a time: the
+        // tiles the epilogue reads (SwiGLU backward: the saved H1 and H3;
+        // accumulate: C itself) come into the (now idle) ring by LDS DMA with
+        // every load of the pass in flight at once, each lane combines its
+        // accumulators with the values at the same places in place (dA, H1, H3
+        // -> dH1, dH3; or C + acc), and the tiles leave in 16-byte row chunks.
+        // Rows are unpadded; 16-byte chunk c of tile row r sits at chunk
+        // c ^ (r % 16), which keeps the lanes' 8-byte reads (32 rows, one
+        // column) and the row reads free of bank conflicts.
+        constexpr int NA = EPI == EPI_SWIGLU_BWD ? 2 : 1;  // tiles read and written
         constexpr int kRowB = BN * 2;
         constexpr int kCpr = BN / 8;
         static_assert(kCpr >= 16 && (kCpr & (kCpr - 1)) == 0, "the chunk swizzle needs 16, 32, ... chunks a row");
-        // wave rows per pass: all of them if both tiles fit the ring, else half, else one
-        constexpr int WPP = 2 * BM * kRowB <= S * kStage                       ? WGM
-                            : (WGM % 2 == 0 && BM * kRowB <= S * kStage)       ? WGM / 2
-                                                                               : 1;
+        // wave rows per pass: all of them if the tiles fit the ring, else half, else one
+        constexpr int WPP = NA * BM * kRowB <= S * kStage                         ? WGM
+                            : (WGM % 2 == 0 && NA * BM / 2 * kRowB <= S * kStage) ? WGM / 2
+                                                                                  : 1;
         constexpr int kPass = WGM / WPP, RP = WPP * WTM;
-        static_assert(2 * RP * kRowB <= S * kStage, "H1/H3 tiles of a pass must fit the ring");
+        static_assert(NA * RP * kRowB <= S * kStage, "the tiles of a pass must fit the ring");
         constexpr int kBlk = RP * kRowB / 1024;  // 1 KiB loads per tile and pass
         static_assert(kBlk % NW == 0, "whole loads per wave");
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
         typedef float f4_t __attribute__((ext_vector_type(4)));
         char *const t1 = smem, *const t3 = smem + RP * kRowB;
-        // the saved rows of this tile; rows past the group's end read as zeros
+        // the rows read back (this tile's; rows past the group's end read as zeros)
+        const bf16_t *const rsrc_base = EPI == EPI_SWIGLU_BWD ? static_cast<const bf16_t *>(p.aux)
+                                                              : static_cast<const bf16_t *>(p.C0);
+        const int64_t ld_in = EPI == EPI_SWIGLU_BWD ? p.ld_aux : p.ldc;
         const __amdgpu_buffer_rsrc_t raux =
-            make_rsrc(static_cast<const bf16_t *>(p.aux) + (q.crow + m0) * p.ld_aux,
-                      static_cast<int64_t>(t.Mg - m0) * p.ld_aux * 2);
-        __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.crow * p.ldc;
+            make_rsrc(rsrc_base + (EPI == EPI_ACCUM ? q.coff : 0) + (q.crow + m0) * ld_in,
+                      static_cast<int64_t>(t.Mg - m0) * ld_in * 2);
+        __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.coff + q.crow * p.ldc;
         __syncthreads();  // every wave is done with the ring
         for (int pass = 0; pass < kPass; ++pass) {
 #pragma unroll
@@ -1094,10 +832,11 @@ void gemm_dma_kernel(GemmArgs p) {
                 const int o = blk * 1024 + lane * 16;
                 const int row = o / kRowB, c = ((o % kRowB) / 16) ^ (row & 15);
                 const int col = n0 + 8 * c;
-                const int off = static_cast<int>(((pass * RP + row) * p.ld_aux + col) * 2);
+                const int off = static_cast<int>(((pass * RP + row) * ld_in + col) * 2);
                 const bool ok = col < p.N;
                 lds_dma16(raux, ok ? off : kOob, sbase + blk * 1024);
-                lds_dma16(raux, ok ? off + static_cast<int>(p.hoff * 2) : kOob, sbase + RP * kRowB + blk * 1024);
+                if constexpr (NA == 2)
+                    lds_dma16(raux, ok ? off + static_cast<int>(p.hoff * 2) : kOob, sbase + RP * kRowB + blk * 1024);
             }
             wait_vmem<0>();
             __syncthreads();
@@ -1112,18 +851,26 @@ void gemm_dma_kernel(GemmArgs p) {
                             const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
                             const int at = row * kRowB + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7);
                             bf4_t *p1 = reinterpret_cast<bf4_t *>(t1 + at);
-                            bf4_t *p3 = reinterpret_cast<bf4_t *>(t3 + at);
-                            const f4_t h1 = __builtin_convertvector(*p1, f4_t), h3 = __builtin_convertvector(*p3, f4_t);
-                            f4_t g1, g3;
+                            const f4_t h1 = __builtin_convertvector(*p1, f4_t);
+                            if constexpr (NA == 2) {
+                                bf4_t *p3 = reinterpret_cast<bf4_t *>(t3 + at);
+                                const f4_t h3 = __builtin_convertvector(*p3, f4_t);
+                                f4_t g1, g3;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float v0 = acc[0][i][j][4 * g + r];
-                                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
-                                g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
-                                g3[r] = v0 * h1[r] * sg;
+                                for (int r = 0; r < 4; ++r) {
+                                    const float v0 = acc[0][i][j][4 * g + r];
+                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
+                                    g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
+                                    g3[r] = v0 * h1[r] * sg;
+                                }
+                                *p1 = __builtin_convertvector(g1, bf4_t);
+                                *p3 = __builtin_convertvector(g3, bf4_t);
+                            } else {
+                                f4_t c1;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) c1[r] = h1[r] + acc[0][i][j][4 * g + r];
+                                *p1 = __builtin_convertvector(c1, bf4_t);
                             }
-                            *p1 = __builtin_convertvector(g1, bf4_t);
-                            *p3 = __builtin_convertvector(g3, bf4_t);
                         }
             }
             __syncthreads();
@@ -1134,8 +881,9 @@ void gemm_dma_kernel(GemmArgs p) {
                 if (m < t.Mg && n < p.N) {
                     const int at = row * kRowB + 16 * (c8 ^ (row & 15));
                     *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) = *reinterpret_cast<const uint4 *>(t1 + at);
-                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
-                        *reinterpret_cast<const uint4 *>(t3 + at);
+                    if constexpr (NA == 2)
+                        *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
+                            *reinterpret_cast<const uint4 *>(t3 + at);
                 }
             }
             if (pass + 1 < kPass) __syncthreads();

@@ -297,8 +297,10 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
         a.ldb = E;
         a.C0 = dx;
         a.ldc = d;
-        err = dt == kBF16 ? launch_gemm_mfma<128, 128, 64, 2, 2, 1, true, true, EPI_ACCUM, bf16_t>(a, s)
-                          : launch_gemm_f32<1, true, true, EPI_ACCUM>(a, s);
+        // bf16 (E is a multiple of 8): the pipelined kernel, whose epilogue brings
+        // the dx tile into LDS by DMA, adds and writes it back in row chunks
+        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_ACCUM>(a, s)
+                          : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_ACCUM, bf16_t, 2>(a, s);
         if (err != hipSuccess) return err;
     }
     // partial[s] = x[chunk s]^T . dz[chunk s] : A(m=i, k=t) = x[t*d + i], B(k=t, n=e) = dz[t*E + e]
@@ -318,8 +320,8 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
     b.C0 = part;
     b.ldc = E;
     b.c_gstride = static_cast<int64_t>(d) * E;
-    err = dt == kBF16 ? launch_gemm_mfma<128, 64, 64, 2, 2, 1, false, false, EPI_STORE, float>(b, s)
-                      : launch_gemm_f32<1, false, false, EPI_STORE>(b, s);
+    err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(b, s)
+                      : launch_gemm_dma<128, 64, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(b, s);
     if (err != hipSuccess) return err;
     const int64_t n = static_cast<int64_t>(d) * E;
     const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096));
