@@ -58,7 +58,7 @@ __device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int6
 // BY_NODE (a compile-time copy of the same code) only names the pilot build's
 // launches apart from the buffer build's in a profile.
 template <bool BY_NODE>
-__global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
+__global__ __launch_bounds__(kChunk) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
                                                         int div, int32_t *__restrict__ counts) {
     __shared__ uint32_t bm[kMaxE * kWords];
     build_bitmap(bm, ids, T, E, k, div);
@@ -71,43 +71,65 @@ __global__ __launch_bounds__(256) void pft_count_kernel(const int32_t *__restric
     }
 }
 
-// One block of 1024 threads; thread e owns expert e.
+// One block of 1024 threads.  Each key (expert or node) gets P = min(64,
+// 1024 / E_p) consecutive lanes of one wave (E_p = E rounded up to a power of
+// two); lane `part` of key e sums the counts of its range of token blocks with
+// independent loads, a segmented scan over the key's lanes places the ranges,
+// and a block-wide scan over the key totals gives the key offsets.
 template <bool BY_NODE>
 __global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restrict__ counts, int nblk, int E,
                                                         int32_t *__restrict__ base, int32_t *__restrict__ tpe,
                                                         int32_t *__restrict__ offsets) {
     __shared__ int wave_tot[16];
-    const int e = threadIdx.x;
-    int total = 0;
-    if (e < E)
-        for (int b = 0; b < nblk; ++b) {
-            const int64_t i = static_cast<int64_t>(b) * E + e;
-            base[i] = total;
-            total += counts[i];
-        }
-    // exclusive scan of `total` over e: within each wave, then across waves
-    const int lane = e & 63, wv = e >> 6;
-    int inc = total;
+    int ep = 1;
+    while (ep < E) ep <<= 1;
+    const int P = min(64, 1024 / ep);
+    const int e = threadIdx.x / P, part = threadIdx.x % P;
+    const bool live = e < E;
+    const int per = (nblk + P - 1) / P;
+    const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+    int mine = 0;
+    if (live)
+        for (int b = b0; b < b1; ++b) mine += counts[static_cast<int64_t>(b) * E + e];
+    // segmented scan over the key's P lanes (P divides 64, so they share a wave)
+    int inc = mine;
+    for (int off = 1; off < P; off <<= 1) {
+        const int v = __shfl_up(inc, off, P);
+        if (part >= off) inc += v;
+    }
+    const int total = __shfl(inc, P - 1, P);  // the key's count
+    const int before_part = inc - mine;
+    // exclusive scan of the key totals: lane part 0 of each key contributes
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int v0 = part == 0 && live ? total : 0;
+    int winc = v0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += v;
+        const int v = __shfl_up(winc, off, 64);
+        if (lane >= off) winc += v;
     }
-    if (lane == 63) wave_tot[wv] = inc;
+    if (lane == 63) wave_tot[wv] = winc;
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wv; ++w) before += wave_tot[w];
-    const int off_e = before + inc - total;
-    if (e < E) {
-        tpe[e] = total;
-        offsets[e] = off_e;
-        if (e == E - 1) offsets[E] = off_e + total;
-        for (int b = 0; b < nblk; ++b) base[static_cast<int64_t>(b) * E + e] += off_e;
+    const int off_e = __shfl(before + winc - v0, 0, P);  // the key's offset, from its lane 0
+    if (live) {
+        if (part == 0) {
+            tpe[e] = total;
+            offsets[e] = off_e;
+            if (e == E - 1) offsets[E] = off_e + total;
+        }
+        int run = off_e + before_part;
+        for (int b = b0; b < b1; ++b) {
+            const int64_t i = static_cast<int64_t>(b) * E + e;
+            base[i] = run;
+            run += counts[i];
+        }
     }
 }
 
 template <bool BY_NODE>
-__global__ __launch_bounds__(256) void pft_scatter_kernel(const int32_t *__restrict__ ids,
+__global__ __launch_bounds__(kChunk) void pft_scatter_kernel(const int32_t *__restrict__ ids,
                                                           const float *__restrict__ wt, int64_t T, int E, int k,
                                                           int div, const int32_t *__restrict__ base,
                                                           int32_t *__restrict__ tok, int32_t *__restrict__ eid,
@@ -158,7 +180,7 @@ hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int 
     int32_t *counts = static_cast<int32_t *>(ws);
     int32_t *base = counts + nblk * nk;
     if (nblk > 0) {
-        hipLaunchKernelGGL(pft_count_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, T, E, k, div,
+        hipLaunchKernelGGL(pft_count_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, T, E, k, div,
                            counts);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -167,7 +189,7 @@ hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int 
                        count_per_key, offsets);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
-    hipLaunchKernelGGL(pft_scatter_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, ids, w, T, E, k, div,
+    hipLaunchKernelGGL(pft_scatter_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, w, T, E, k, div,
                        base, tok, keyid, cw, s2r);
     return hipGetLastError();
 }
