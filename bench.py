@@ -119,14 +119,32 @@ def main():
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    per_step = [ev0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
+
+    # the same steps with the 256 MB Infinity Cache flushed before each one (a
+    # 1 GiB scratch write outside the step's events), so no input is served
+    # from the last step's cache contents
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flushed = []
+    for _ in range(min(args.steps, 10)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        flushed.append(a.elapsed_time(b))
+    del flush
     ms = max(gpu_ms, wall * 1e3 / args.steps)
     flops = wl.useful_flops()
     tflops = flops["total"] / (ms * 1e-3) / 1e12
@@ -201,6 +219,7 @@ def main():
                       "h13": "recomputed" if args.lean else "saved",
                       "shared_experts": "side stream" if layer.shared and layer.overlap else "in order"},
            "tokens_per_s": round(tok_s, 1), "gpu_ms_per_step": round(gpu_ms, 4),
+           "step_ms": pctl(per_step), "step_ms_cache_flushed": pctl(flushed),
            "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
            "useful_gflop_per_step": round(flops["total"] / 1e9, 2),
            "saved_activation_mb": round(layer.saved_bytes() / 1e6, 1),
@@ -209,8 +228,16 @@ def main():
 
     out["ep_rbd"] = ep_rbd(xm, wl, layer, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_sample_tokens)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(wl, inp, args.cpu_sample_tokens, layer)
     print(json.dumps(out), flush=True)
+
+
+def pctl(v):
+    """median, p10 and p90 of a list of step times (ms)."""
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
 
 
 def ep_rbd(xm, wl, layer, stream, nodes=8, ranks=8, n_rep=20):
@@ -268,10 +295,13 @@ def ep_rbd(xm, wl, layer, stream, nodes=8, ranks=8, n_rep=20):
             "regroup": {"rows": n, "d": d, "us": round(t_reg, 2), "GB_per_s": round(moved / (t_reg * 1e-6) / 1e9, 1)}}
 
 
-def cpu_baseline(wl, inp, sample_tokens):
+def cpu_baseline(wl, inp, sample_tokens, layer):
     """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
     same inputs: full forward and backward (routing, experts, shared experts,
-    combine, all gradients) for those tokens; throughput scaled per token."""
+    combine, all gradients) for those tokens; throughput scaled per token.
+    Its y and dx of those tokens also check the GPU run's own outputs (both are
+    per token): normwise relative error over the tokens whose top-k agrees with
+    the oracle's (a near-tie may order two experts differently)."""
     import numpy as np
     import torch
 
@@ -292,13 +322,23 @@ def cpu_baseline(wl, inp, sample_tokens):
     o["dy"] = o["dy"][:n]
     t0 = time.perf_counter()
     fwd = orc.layer_forward(o, wl.k, 1, wl.inv_tau, n_shared=wl.n_shared)
-    orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared)
+    bwd = orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared)
     dt = time.perf_counter() - t0
     sub = wl.__class__(**{**wl.__dict__, "T": n})
     fl = sub.useful_flops()["total"]
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS", "cores": orc.get_threads(), "kind": "oracle",
+    base = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS", "cores": orc.get_threads(), "kind": "oracle",
             "sample": f"{n} of {wl.T} tokens, full forward+backward incl. all weight gradients",
             "seconds": round(dt, 2), "tokens_per_s": round(n / dt, 2)}
+    ok = (layer.topk_ids[:n].cpu().numpy() == fwd["route"]["topk_ids"]).all(axis=1)
+
+    def rel(g, r):
+        g = g[:n].detach().cpu().to(torch.float64).numpy()[ok]
+        return float(np.linalg.norm(g - r[ok]) / max(np.linalg.norm(r[ok]), 1e-300))
+    ry, rdx = rel(layer.y, fwd["y"]), rel(layer.dx, bwd["dx"])
+    tol = 2e-2
+    parity = {"tokens": n, "tokens_compared": int(ok.sum()), "y_rel_err": ry, "dx_rel_err": rdx, "rtol": tol,
+              "pass": bool(ry <= tol and rdx <= tol), "against": "oracle (fp64) on the same inputs"}
+    return base, parity
 
 
 if __name__ == "__main__":
