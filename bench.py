@@ -206,10 +206,19 @@ def main():
         tot_ms += t
         tot_flop += fl
     achieved = tot_flop / (tot_ms * 1e-3) / 1e12
+    # the same launches against HBM: each operand read once (the gathered rows,
+    # the weights) and each output written once (act, H1|H3)
+    up_bytes = [2.0 * (R * d + 2 * wl.E * d * h + R * h + R * 2 * h)]
+    if layer.shared:
+        up_bytes.append(2.0 * (wl.T * d + 2 * d * layer.hs + wl.T * layer.hs + wl.T * 2 * layer.hs))
+    hbm_gbps = sum(up_bytes) / (tot_ms * 1e-3) / 1e9
     roofline = {"kernel": "gemm_dma_kernel<128,128,32,2,2,2,...,EPI_SWIGLU> (expert up-projection, DeepSeek-MoE-16B tile)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
-                "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches)}
+                "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches),
+                "hbm": {"algorithmic_bytes_per_launch": round(sum(up_bytes) / len(up_bytes)),
+                        "achieved_GBps": round(hbm_gbps, 1), "peak_GBps": 8000.0,
+                        "frac": round(hbm_gbps / 8000.0, 4)}}
 
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
