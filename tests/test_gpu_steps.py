@@ -195,6 +195,9 @@ FFN_CASES = [
     # d and h off every tile multiple: partial k blocks in all six products,
     # partial m/n tiles in the weight gradients
     ("bf16", 517, 328, 264, 7, 0.3),
+    # every row on expert 0, seven empty experts; the mean of 1500 rows per
+    # expert selects the 256-row tiles
+    ("bf16", 12000, 256, 192, 8, 1.0),
 ]
 
 
@@ -340,6 +343,26 @@ def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
     assert_wgrad_close(host(dw1), ref["dw1"], rows, lambda e: floors(e)[0], rt, "dw1")
     assert_wgrad_close(host(dw3), ref["dw3"], rows, lambda e: floors(e)[1], rt, "dw3")
     assert_wgrad_close(host(dw2), ref["dw2"], rows, lambda e: floors(e)[2], rt, "dw2")
+
+
+def test_expert_ffn_zero_rows(xm):
+    """No rows at all: nothing to compute, and every weight gradient is zero."""
+    E, d, h = 4, 128, 64
+    bf = torch.bfloat16
+    off = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    w1 = torch.randn((E, d, h), device="cuda").to(bf)
+    w3 = torch.randn((E, d, h), device="cuda").to(bf)
+    w2 = torch.randn((E, h, d), device="cuda").to(bf)
+    e = lambda *s: torch.empty(s, dtype=bf, device="cuda")
+    act, h13, ye = e(0, h), e(0, 2 * h), e(0, d)
+    xm.xmoe_expert_ffn(e(0, d), w1, w3, w2, off, act, ye, h13=h13)
+    dw1 = torch.full((E, d, h), float("nan"), dtype=bf, device="cuda")
+    dw3 = torch.full((E, d, h), float("nan"), dtype=bf, device="cuda")
+    dw2 = torch.full((E, h, d), float("nan"), dtype=bf, device="cuda")
+    xm.xmoe_expert_ffn_bwd(e(0, d), w1, w3, w2, act, h13, e(0, d), off, e(0, 2 * h), e(0, d), dw1, dw3, dw2)
+    torch.cuda.synchronize()
+    for t in (dw1, dw3, dw2):
+        assert torch.equal(t, torch.zeros_like(t))
 
 
 # ------------------------------------------------------------------ router backward
