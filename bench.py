@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the shared experts in order on the main stream")
+    ap.add_argument("--merge-shared", action="store_true",
+                    help="carry the shared experts as always-routed experts in the routed buffer")
     ap.add_argument("--lean", action="store_true",
                     help="recompute H1/H3 in the backward instead of keeping them from the forward")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
@@ -107,7 +109,7 @@ def main():
     weights = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias")
                if k in inp}
     layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=args.lean,
-                           overlap=not args.no_overlap)
+                           overlap=not args.no_overlap, merge_shared=args.merge_shared)
     x, dy = inp["x"], inp["dy"]
     stream = torch.cuda.current_stream()
 
@@ -181,15 +183,19 @@ def main():
     # roofline of the dominant kernel: the up-projection (W1|W3 + SwiGLU), launched
     # once for the routed experts (rows gathered from x through the PFT's
     # token_ids) and once for the shared experts per step
-    R, d, h = wl.R, wl.d, wl.h
-    up_launches = [(lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, weights["w1"], weights["w3"],
+    # (with the shared experts merged into the buffer: one launch over the
+    # routed and shared experts together)
+    R, d, h = layer.R, wl.d, wl.h
+    up_launches = [(lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, layer.W1, layer.W3,
                                                         layer.pft.expert_offsets, layer.act, layer.h13),
                     4.0 * R * d * h)]
-    if layer.shared:
+    up_bytes = [2.0 * (R * d + 2 * layer.Ec * d * h + R * h + R * 2 * h)]
+    if layer.side_shared:
         hs = layer.hs
         up_launches.append((lambda: xm.xmoe_expert_ffn_up(x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0),
                                                           layer.sh_off, layer.sh_act, layer.sh_h13),
                             4.0 * wl.T * d * hs))
+        up_bytes.append(2.0 * (wl.T * d + 2 * d * hs + wl.T * hs + wl.T * 2 * hs))
     n_rep = 20
     tot_ms, tot_flop, per = 0.0, 0.0, []
     for (launch, fl) in up_launches:
@@ -208,9 +214,6 @@ def main():
     achieved = tot_flop / (tot_ms * 1e-3) / 1e12
     # the same launches against HBM: each operand read once (the gathered rows,
     # the weights) and each output written once (act, H1|H3)
-    up_bytes = [2.0 * (R * d + 2 * wl.E * d * h + R * h + R * 2 * h)]
-    if layer.shared:
-        up_bytes.append(2.0 * (wl.T * d + 2 * d * layer.hs + wl.T * layer.hs + wl.T * 2 * layer.hs))
     hbm_gbps = sum(up_bytes) / (tot_ms * 1e-3) / 1e9
     roofline = {"kernel": "gemm_dma_kernel<128,128,32,2,2,2,...,EPI_SWIGLU> (expert up-projection, DeepSeek-MoE-16B tile)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -226,7 +229,9 @@ def main():
            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "h": wl.h, "k": wl.k,
                       "n_shared": wl.n_shared, "h_shared": wl.h_shared, "passes": "fwd+bwd",
                       "h13": "recomputed" if args.lean else "saved",
-                      "shared_experts": "side stream" if layer.shared and layer.overlap else "in order"},
+                      "shared_experts": ("merged as always-routed experts" if layer.merged else
+                                         "side stream" if layer.side_shared and layer.overlap else
+                                         "in order" if layer.shared else "none")},
            "tokens_per_s": round(tok_s, 1), "gpu_ms_per_step": round(gpu_ms, 4),
            "step_ms": pctl(per_step), "step_ms_cache_flushed": pctl(flushed),
            "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
@@ -282,7 +287,9 @@ def ep_rbd(xm, wl, layer, stream, nodes=8, ranks=8, n_rep=20):
     n_pilots = int(no[-1].item())
 
     sc, sd = torch.empty((ranks,), **i32), torch.empty((ranks + 1,), **i32)
-    t_send = timed(lambda: xm.xmoe_ep_send_plan(layer.pft.expert_offsets, ranks, sc, sd))
+    # the routed experts' part of the buffer (shared experts stay on every rank)
+    routed_off = layer.pft.expert_offsets[:E + 1]
+    t_send = timed(lambda: xm.xmoe_ep_send_plan(routed_off, ranks, sc, sd))
 
     el = E // ranks
     C = torch.stack([torch.bincount(workloads.random_topk(T, E, k, seed=100 + s)[0].reshape(-1).long(),

@@ -149,6 +149,22 @@ xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t
                            void *stream);
 
 /*
+ * The same buffer with shared experts carried as experts every token is
+ * routed to with weight 1 (the shared expert beside the routed ones of
+ * "5.4 MoE模型在分布式训练中的应用", section 实际案例, held in the X-MoE
+ * article's section 2.1.1 buffer): E_routed + n_shared experts; each
+ * token has its k routed slots (topk_ids, topk_w [T,k], ids in [0, E_routed);
+ * others are skipped) followed by n_shared slots for experts
+ * E_routed .. E_routed + n_shared - 1, weight 1.  The pft is sized as for
+ * E = E_routed + n_shared experts and k + n_shared slots per token (rows
+ * R = T*(k + n_shared); slot_to_row [T, k + n_shared]).  workspace:
+ * >= xmoe_build_pft_workspace_size(T, E_routed + n_shared, k + n_shared).
+ */
+xmoe_status xmoe_build_pft_shared(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E_routed,
+                                  int32_t k, int32_t n_shared, const xmoe_pft *pft, void *workspace,
+                                  size_t ws_bytes, void *stream);
+
+/*
  * Dispatch = the PFT gather (X-MoE article, section 2.1.2):
  *   xs[r, :] = x[token_ids[r], :]   for every PFT row r     (xs [R,d])
  * Carried out token by token through slot_to_row (each input row is read once
@@ -310,11 +326,15 @@ size_t xmoe_route_bwd_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype
  *   dwg = x^T . dz               (fp32 [d,E], fixed-order split-T sum)
  * With XMOE_BF16, dz is rounded to bf16 for the two matrix-core products
  * (fp32 accumulation).  workspace: device, >= xmoe_route_bwd_workspace_size.
+ * dtopk_w: row t at dtopk_w + t*ldw (ldw >= k; ldw > k reads the routed slots
+ * of a buffer with more slots per token, such as one that also holds shared
+ * experts).  accumulate != 0: dx += dz . wg^T as above; 0: dx = dz . wg^T.
  */
 xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits,
-                           const int32_t *topk_ids, const float *dtopk_w, xmoe_dtype dtype,
+                           const int32_t *topk_ids, const float *dtopk_w, int32_t ldw, xmoe_dtype dtype,
                            int64_t T, int32_t d, int32_t E, int32_t k, float inv_temperature,
-                           void *dx, float *dwg, void *workspace, size_t ws_bytes, void *stream);
+                           int32_t accumulate, void *dx, float *dwg, void *workspace, size_t ws_bytes,
+                           void *stream);
 
 /* ------------------------------------------------------------------------
  * Pilot tokens of Redundancy-Bypassing Dispatch, stage 1

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "XmoeError", "PFT", "lib_path", "xmoe_version", "xmoe_query_device", "xmoe_route",
     "xmoe_route_workspace_size",
-    "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_dispatch", "xmoe_expert_ffn_up",
+    "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_build_pft_shared", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
     "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13",
@@ -82,8 +82,9 @@ _lib_bwd_dw2 = _sig("xmoe_expert_ffn_bwd_dw2", [_vp, _vp, ctypes.c_int, _vp, _i3
 _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp,
                                                _vp, _vp])
 _lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
-_lib_rbwd = _sig("xmoe_route_bwd", [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp,
-                                    _vp, _vp, _sz, _vp])
+_lib_rbwd = _sig("xmoe_route_bwd", [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int, _i64, _i32, _i32, _i32, _f32,
+                                    _i32, _vp, _vp, _vp, _sz, _vp])
+_lib_pft_sh = _sig("xmoe_build_pft_shared", [_vp, _vp, _i64, _i32, _i32, _i32, ctypes.POINTER(_CPft), _vp, _sz, _vp])
 _lib_pilots_ws = _sig("xmoe_build_pilots_workspace_size", [_i64, _i32, _i32, _i32], _sz)
 _lib_pilots = _sig("xmoe_build_pilots", [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _lib_ep_send = _sig("xmoe_ep_send_plan", [_vp, _i32, _i32, _vp, _vp, _vp])
@@ -197,6 +198,17 @@ def xmoe_build_pft(topk_ids, topk_w, E: int, pft: PFT, workspace, stream=None):
                     workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_build_pft")
 
 
+def xmoe_build_pft_shared(topk_ids, topk_w, E_routed: int, n_shared: int, pft: PFT, workspace, stream=None):
+    """The buffer with n_shared always-routed experts after the E_routed routed
+    ones (weight 1); pft must be PFT(T, E_routed + n_shared, k + n_shared)."""
+    T, k = topk_ids.shape
+    if pft.k != k + n_shared or pft.E != E_routed + n_shared:
+        raise ValueError("pft must be sized for E_routed + n_shared experts and k + n_shared slots")
+    c = pft.c()
+    _check(_lib_pft_sh(_ptr(topk_ids), _ptr(topk_w), T, E_routed, k, n_shared, ctypes.byref(c), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_build_pft_shared")
+
+
 def xmoe_dispatch(x, k: int, pft: PFT, xs, stream=None):
     T, d = x.shape
     c = pft.c()
@@ -303,12 +315,16 @@ def xmoe_route_bwd_workspace_size(T: int, d: int, E: int, dtype: torch.dtype) ->
 
 
 def xmoe_route_bwd(x, wg, logits, topk_ids, dtopk_w, dx, dwg, workspace, inv_temperature: float = 1.0,
-                   stream=None):
+                   accumulate: bool = True, stream=None):
+    """dtopk_w [T, k] may be the first k columns of a wider [T, k'] buffer
+    (rows of unit stride); accumulate=False writes dx instead of adding to it."""
     T, d = x.shape
     E = wg.shape[1]
     k = topk_ids.shape[1]
-    _check(_lib_rbwd(_ptr(x), _ptr(wg), _ptr(logits), _ptr(topk_ids), _ptr(dtopk_w), _dt(x), T, d, E, k,
-                     inv_temperature, _ptr(dx), _ptr(dwg), _ptr(workspace),
+    if not dtopk_w.is_cuda or dtopk_w.dim() != 2 or dtopk_w.stride(1) != 1 or dtopk_w.shape != (T, k):
+        raise ValueError("dtopk_w must be a [T, k] device tensor with unit column stride")
+    _check(_lib_rbwd(_ptr(x), _ptr(wg), _ptr(logits), _ptr(topk_ids), dtopk_w.data_ptr(), dtopk_w.stride(0), _dt(x),
+                     T, d, E, k, inv_temperature, 1 if accumulate else 0, _ptr(dx), _ptr(dwg), _ptr(workspace),
                      workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_route_bwd")
 
 

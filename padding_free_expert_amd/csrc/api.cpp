@@ -195,8 +195,30 @@ xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t
     REQUIRE(ws_bytes >= xmoe::pft_workspace(T, E), XMOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes,
             xmoe::pft_workspace(T, E));
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_build_pft(topk_ids, topk_w, T, E, k, to_ptrs(pft), workspace, S(stream)),
+    return hip_status(xmoe::launch_build_pft(topk_ids, topk_w, T, E, k, 0, to_ptrs(pft), workspace, S(stream)),
                       "xmoe_build_pft launch");
+}
+
+xmoe_status xmoe_build_pft_shared(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E_routed,
+                                  int32_t k, int32_t n_shared, const xmoe_pft *pft, void *workspace, size_t ws_bytes,
+                                  void *stream) {
+    REQUIRE(n_shared >= 0, XMOE_ERR_INVALID_VALUE, "n_shared must be >= 0");
+    const int64_t E = static_cast<int64_t>(E_routed) + n_shared, ks = static_cast<int64_t>(k) + n_shared;
+    REQUIRE(T == 0 || (topk_ids && topk_w), XMOE_ERR_INVALID_VALUE, "topk_ids and topk_w are required");
+    REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
+    REQUIRE(E_routed >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E_routed >= 1 and E_routed + n_shared <= 1024");
+    REQUIRE(k >= 1 && k <= E_routed, XMOE_ERR_INVALID_VALUE, "k must be in [1, E_routed]");
+    REQUIRE(T * ks <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*(k+n_shared) must be < 2^31");
+    TRY(check_pft(pft, T > 0, T > 0, T > 0));
+    REQUIRE(pft->tokens_per_expert && pft->expert_offsets, XMOE_ERR_INVALID_VALUE,
+            "pft->tokens_per_expert and pft->expert_offsets are required");
+    const size_t need = xmoe::pft_workspace(T, static_cast<int>(E));
+    REQUIRE(workspace && aligned16(workspace), XMOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
+    REQUIRE(ws_bytes >= need, XMOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_build_pft(topk_ids, topk_w, T, static_cast<int>(E), k, n_shared, to_ptrs(pft),
+                                             workspace, S(stream)),
+                      "xmoe_build_pft_shared launch");
 }
 
 xmoe_status xmoe_dispatch(const void *x, xmoe_dtype dtype, int64_t T, int32_t d, int32_t k, const xmoe_pft *pft,
@@ -401,15 +423,17 @@ size_t xmoe_route_bwd_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype
 }
 
 xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
-                           const float *dtopk_w, xmoe_dtype dtype, int64_t T, int32_t d, int32_t E, int32_t k,
-                           float inv_temperature, void *dx, float *dwg, void *workspace, size_t ws_bytes,
-                           void *stream) {
+                           const float *dtopk_w, int32_t ldw, xmoe_dtype dtype, int64_t T, int32_t d, int32_t E,
+                           int32_t k, float inv_temperature, int32_t accumulate, void *dx, float *dwg,
+                           void *workspace, size_t ws_bytes, void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(wg && dwg && (T == 0 || (x && logits && topk_ids && dtopk_w && dx)), XMOE_ERR_INVALID_VALUE,
             "a required pointer is NULL");
     REQUIRE(T >= 0 && T <= kMaxRows && d >= 1, XMOE_ERR_INVALID_VALUE, "T must be in [0, 2^31) and d >= 1");
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
+    REQUIRE(ldw >= k, XMOE_ERR_INVALID_VALUE, "ldw must be >= k");
+    REQUIRE(T * static_cast<int64_t>(ldw) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*ldw must be < 2^31");
     if (dtype == XMOE_BF16) {
         REQUIRE(d % 8 == 0 && E % 8 == 0, XMOE_ERR_UNSUPPORTED, "bf16 needs d and E multiples of 8");
         REQUIRE(aligned16(x) && aligned16(wg) && aligned16(dx), XMOE_ERR_UNSUPPORTED,
@@ -419,8 +443,8 @@ xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits, c
     REQUIRE(workspace && aligned16(workspace), XMOE_ERR_WORKSPACE, "workspace is NULL or not 16-byte aligned");
     REQUIRE(ws_bytes >= need, XMOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_route_bwd(dtype, x, wg, logits, topk_ids, dtopk_w, T, d, E, k, inv_temperature, dx,
-                                             dwg, workspace, S(stream)),
+    return hip_status(xmoe::launch_route_bwd(dtype, x, wg, logits, topk_ids, dtopk_w, ldw, T, d, E, k, inv_temperature,
+                                             accumulate != 0, dx, dwg, workspace, S(stream)),
                       "xmoe_route_bwd launch");
 }
 

@@ -24,12 +24,14 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
 size_t route_workspace(int64_t T, int d, int E, int dt);
 size_t route_bwd_workspace(int64_t T, int d, int E, int dt);
 hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
-                            const float *dtopk_w, int64_t T, int d, int E, int k, float inv_tau, void *dx,
-                            float *dwg, void *ws, hipStream_t s);
+                            const float *dtopk_w, int ldw, int64_t T, int d, int E, int k, float inv_tau,
+                            bool accumulate, void *dx, float *dwg, void *ws, hipStream_t s);
 
 // Padding-Free Token buffer
 size_t pft_workspace(int64_t T, int E);
-hipError_t launch_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k,
+// E experts in all; each token has k routed slots then n_always slots for the
+// last n_always experts, weight 1
+hipError_t launch_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k, int n_always,
                             const PftPtrs &pft, void *ws, hipStream_t s);
 
 // pilot tokens (Redundancy-Bypassing Dispatch, stage 1); workspace pft_workspace(T, E / experts_per_node)

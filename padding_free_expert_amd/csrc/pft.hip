@@ -25,6 +25,10 @@
 // that node -- the per-node deduplication -- so the rows are the (token, node)
 // pilots, listed by node, then token, and every slot of a token bound for one
 // node gets the same pilot row.
+//
+// Shared experts can ride in the same buffer as experts every token is routed
+// to with weight 1: with n_always > 0 each token has, after its k routed slots,
+// n_always more slots for the last n_always experts (E - n_always + i).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,7 +43,15 @@ constexpr int kMaxE = 1024;
 // key of an expert id: e / div (div = 1: the expert; experts per node: the node)
 __device__ __forceinline__ int key_of(int e, int div) { return div == 1 ? e : e / div; }
 
-__device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int64_t T, int E, int k, int div) {
+// expert of slot j of token t: routed slots from ids, then the always-routed ones
+__device__ __forceinline__ int slot_expert(const int32_t *__restrict__ ids, int64_t t, int j, int k, int E, int na) {
+    if (j >= k) return E - na + (j - k);
+    const int e = ids[t * k + j];
+    return e < E - na ? e : -1;  // a routed id among the always-routed experts is invalid
+}
+
+__device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int64_t T, int E, int k, int na,
+                             int div) {
     const int nk = E / div;
     for (int i = threadIdx.x; i < nk * kWords; i += blockDim.x) bm[i] = 0u;
     __syncthreads();
@@ -47,8 +59,8 @@ __device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int6
     if (t < T) {
         const uint32_t bit = 1u << (threadIdx.x & 31);
         const int w = threadIdx.x >> 5;
-        for (int j = 0; j < k; ++j) {
-            const int e = ids[t * k + j];
+        for (int j = 0; j < k + na; ++j) {
+            const int e = slot_expert(ids, t, j, k, E, na);
             if (e >= 0 && e < E) atomicOr(&bm[key_of(e, div) * kWords + w], bit);
         }
     }
@@ -59,9 +71,9 @@ __device__ void build_bitmap(uint32_t *bm, const int32_t *__restrict__ ids, int6
 // launches apart from the buffer build's in a profile.
 template <bool BY_NODE>
 __global__ __launch_bounds__(kChunk) void pft_count_kernel(const int32_t *__restrict__ ids, int64_t T, int E, int k,
-                                                        int div, int32_t *__restrict__ counts) {
+                                                           int na, int div, int32_t *__restrict__ counts) {
     __shared__ uint32_t bm[kMaxE * kWords];
-    build_bitmap(bm, ids, T, E, k, div);
+    build_bitmap(bm, ids, T, E, k, na, div);
     const int nk = E / div;
     for (int e = threadIdx.x; e < nk; e += blockDim.x) {
         int c = 0;
@@ -131,19 +143,20 @@ __global__ __launch_bounds__(1024) void pft_scan_kernel(const int32_t *__restric
 template <bool BY_NODE>
 __global__ __launch_bounds__(kChunk) void pft_scatter_kernel(const int32_t *__restrict__ ids,
                                                           const float *__restrict__ wt, int64_t T, int E, int k,
-                                                          int div, const int32_t *__restrict__ base,
+                                                          int na, int div, const int32_t *__restrict__ base,
                                                           int32_t *__restrict__ tok, int32_t *__restrict__ eid,
                                                           float *__restrict__ cw, int32_t *__restrict__ s2r) {
     __shared__ uint32_t bm[kMaxE * kWords];
-    build_bitmap(bm, ids, T, E, k, div);
+    build_bitmap(bm, ids, T, E, k, na, div);
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kChunk + threadIdx.x;
     if (t >= T) return;
-    const int64_t R = T * k;
+    const int ks = k + na;  // slots per token
+    const int64_t R = T * ks;
     const int nk = E / div;
     const int wd = threadIdx.x >> 5;
     const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
-    for (int j = 0; j < k; ++j) {
-        const int e = ids[t * k + j];
+    for (int j = 0; j < ks; ++j) {
+        const int e = slot_expert(ids, t, j, k, E, na);
         int64_t r = -1;
         int key = -1;
         if (e >= 0 && e < E) {
@@ -153,11 +166,11 @@ __global__ __launch_bounds__(kChunk) void pft_scatter_kernel(const int32_t *__re
             r = base[static_cast<int64_t>(blockIdx.x) * nk + key] + rank;
             if (r >= R) r = -1;
         }
-        s2r[t * k + j] = static_cast<int32_t>(r);
+        s2r[t * ks + j] = static_cast<int32_t>(r);
         if (r >= 0) {  // a token's slots bound for one key write the same row with the same values
             if (tok) tok[r] = static_cast<int32_t>(t);
             if (eid) eid[r] = key;
-            if (cw) cw[r] = wt ? wt[t * k + j] : 0.0f;
+            if (cw) cw[r] = j >= k ? 1.0f : (wt ? wt[t * k + j] : 0.0f);
         }
     }
 }
@@ -173,15 +186,16 @@ namespace {
 
 // Stable counting sort of the slots by key (expert, or node when div > 1).
 template <bool BY_NODE>
-hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int k, int div, int32_t *tok, int32_t *keyid,
+hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int k, int na, int div, int32_t *tok,
+                      int32_t *keyid,
                       int32_t *count_per_key, int32_t *offsets, float *cw, int32_t *s2r, void *ws, hipStream_t s) {
     const int64_t nblk = (T + kChunk - 1) / kChunk;
     const int nk = E / div;
     int32_t *counts = static_cast<int32_t *>(ws);
     int32_t *base = counts + nblk * nk;
     if (nblk > 0) {
-        hipLaunchKernelGGL(pft_count_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, T, E, k, div,
-                           counts);
+        hipLaunchKernelGGL(pft_count_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, T, E, k, na,
+                           div, counts);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -189,22 +203,22 @@ hipError_t keyed_sort(const int32_t *ids, const float *w, int64_t T, int E, int 
                        count_per_key, offsets);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nblk == 0) return err;
-    hipLaunchKernelGGL(pft_scatter_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, w, T, E, k, div,
-                       base, tok, keyid, cw, s2r);
+    hipLaunchKernelGGL(pft_scatter_kernel<BY_NODE>, dim3(static_cast<unsigned>(nblk)), dim3(kChunk), 0, s, ids, w, T, E, k, na,
+                       div, base, tok, keyid, cw, s2r);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, const PftPtrs &pft, void *ws,
-                            hipStream_t s) {
-    return keyed_sort<false>(ids, w, T, E, k, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
+hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E, int k, int n_always,
+                            const PftPtrs &pft, void *ws, hipStream_t s) {
+    return keyed_sort<false>(ids, w, T, E, k, n_always, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
                       pft.combine_weights, pft.slot_to_row, ws, s);
 }
 
 hipError_t launch_build_pilots(const int32_t *ids, int64_t T, int E, int k, int experts_per_node,
                                const PilotPtrs &pl, void *ws, hipStream_t s) {
-    return keyed_sort<true>(ids, nullptr, T, E, k, experts_per_node, pl.pilot_token_ids, pl.pilot_node_ids, pl.node_counts,
+    return keyed_sort<true>(ids, nullptr, T, E, k, 0, experts_per_node, pl.pilot_token_ids, pl.pilot_node_ids, pl.node_counts,
                       pl.node_offsets, nullptr, pl.slot_to_pilot, ws, s);
 }
 

@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
 template <int Q, typename OutT>
 __global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__ logits,
                                                        const int32_t *__restrict__ ids,
-                                                       const float *__restrict__ dw, int64_t T, int E, int k,
-                                                       float inv_tau, OutT *__restrict__ dz) {
+                                                       const float *__restrict__ dw, int ldw, int64_t T, int E,
+                                                       int k, float inv_tau, OutT *__restrict__ dz) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__
     den = wave_sum(den);
     for (int j = 0; j < k; ++j) {
         const int ej = ids[t * k + j];
-        const float gj = dw[t * k + j];
+        const float gj = dw[t * ldw + j];
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if (lane + 64 * q == ej) g[q] = gj;
@@ -258,19 +258,19 @@ size_t route_bwd_workspace(int64_t T, int d, int E, int dt) {
 
 template <typename OutT>
 static void launch_dz(int E, dim3 grid, hipStream_t s, const float *logits, const int32_t *ids, const float *dw,
-                      int64_t T, int k, float inv_tau, OutT *dz) {
+                      int ldw, int64_t T, int k, float inv_tau, OutT *dz) {
     switch (q_of(E)) {
-        case 1: hipLaunchKernelGGL((route_dz_kernel<1, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
-        case 2: hipLaunchKernelGGL((route_dz_kernel<2, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
-        case 4: hipLaunchKernelGGL((route_dz_kernel<4, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
-        case 8: hipLaunchKernelGGL((route_dz_kernel<8, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
-        default: hipLaunchKernelGGL((route_dz_kernel<16, OutT>), grid, dim3(256), 0, s, logits, ids, dw, T, E, k, inv_tau, dz); break;
+        case 1: hipLaunchKernelGGL((route_dz_kernel<1, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
+        case 2: hipLaunchKernelGGL((route_dz_kernel<2, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
+        case 4: hipLaunchKernelGGL((route_dz_kernel<4, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
+        case 8: hipLaunchKernelGGL((route_dz_kernel<8, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
+        default: hipLaunchKernelGGL((route_dz_kernel<16, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
     }
 }
 
 hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
-                            const float *dtopk_w, int64_t T, int d, int E, int k, float inv_tau, void *dx,
-                            float *dwg, void *ws, hipStream_t s) {
+                            const float *dtopk_w, int ldw, int64_t T, int d, int E, int k, float inv_tau,
+                            bool accumulate, void *dx, float *dwg, void *ws, hipStream_t s) {
     const int S = rbwd_splits(T, d, E);
     const size_t dz_bytes = align256(static_cast<size_t>(T) * E * (dt == kBF16 ? 2 : 4));
     void *dz = ws;
@@ -278,11 +278,14 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
     hipError_t err;
     if (T > 0) {
         const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves));
-        if (dt == kBF16) launch_dz<bf16_t>(E, grid, s, logits, topk_ids, dtopk_w, T, k, inv_tau, static_cast<bf16_t *>(dz));
-        else launch_dz<float>(E, grid, s, logits, topk_ids, dtopk_w, T, k, inv_tau, static_cast<float *>(dz));
+        if (dt == kBF16)
+            launch_dz<bf16_t>(E, grid, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<bf16_t *>(dz));
+        else
+            launch_dz<float>(E, grid, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<float *>(dz));
         if ((err = hipGetLastError()) != hipSuccess) return err;
 
-        // dx[t] += dz[t] . Wg^T : A = dz [T,E] (k-contiguous), B(k=e, n=i) = Wg[i*E + e]
+        // dx[t] += dz[t] . Wg^T (or dx[t] = ... without accumulate) : A = dz [T,E]
+        // (k-contiguous), B(k=e, n=i) = Wg[i*E + e]
         GemmArgs a{};
         a.group_mode = GM_ROWS;
         a.G = 1;
@@ -299,8 +302,12 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
         a.ldc = d;
         // bf16 (E is a multiple of 8): the pipelined kernel, whose epilogue brings
         // the dx tile into LDS by DMA, adds and writes it back in row chunks
-        err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_ACCUM>(a, s)
-                          : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_ACCUM, bf16_t, 2>(a, s);
+        if (accumulate)
+            err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_ACCUM>(a, s)
+                              : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_ACCUM, bf16_t, 2>(a, s);
+        else
+            err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(a, s)
+                              : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_STORE, bf16_t, 2>(a, s);
         if (err != hipSuccess) return err;
     }
     // partial[s] = x[chunk s]^T . dz[chunk s] : A(m=i, k=t) = x[t*d + i], B(k=t, n=e) = dz[t*E + e]

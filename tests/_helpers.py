@@ -154,6 +154,18 @@ def by_expert(ids: np.ndarray, vals: np.ndarray) -> np.ndarray:
     return np.take_along_axis(np.asarray(vals), order, 1)
 
 
+def buffer_routing(layer, ids: np.ndarray, w: np.ndarray):
+    """(ids, w, E) of the routing a layer's buffer holds: the routed slots, then,
+    when the layer carries its shared experts as always-routed ones, one slot
+    per shared expert (experts E .. E+n-1) with weight 1."""
+    if not getattr(layer, "merged", False):
+        return ids, w, layer.E
+    T, ns, E = ids.shape[0], layer.ns, layer.E
+    ids_b = np.concatenate([ids, np.tile(np.arange(E, E + ns, dtype=ids.dtype), (T, 1))], axis=1)
+    w_b = np.concatenate([np.asarray(w, np.float32), np.ones((T, ns), np.float32)], axis=1)
+    return ids_b, w_b, E + ns
+
+
 def pft_invariants(ids: np.ndarray, w: np.ndarray, E: int, pft: dict):
     """Properties every valid Padding-Free Token buffer of routing (ids, w) has:
     T*k rows, each token k times, each (token, expert) once, rows grouped by

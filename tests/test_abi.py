@@ -90,3 +90,13 @@ def test_pilot_and_ep_entry_points_reject_on_host(xm):
     # row scatter: d not a multiple of 8, unknown dtype
     assert xm._lib_scatter_rows(p, 1, 10, 12, p, 10, p, None) == 2
     assert xm._lib_scatter_rows(p, 9, 10, 16, p, 10, p, None) == 2
+
+
+def test_shared_buffer_and_route_bwd_reject_on_host(xm):
+    p = ctypes.c_void_p(16)  # never dereferenced
+    pft = xm._CPft(16, 16, 16, 16, 16, 16)
+    assert xm._lib_pft_sh(p, p, 100, 64, 6, -1, ctypes.byref(pft), p, 1 << 20, None) == 1      # n_shared < 0
+    assert xm._lib_pft_sh(p, p, 100, 1020, 6, 8, ctypes.byref(pft), p, 1 << 20, None) == 1     # > 1024 experts
+    assert xm._lib_pft_sh(p, p, 100000, 64, 6, 2, ctypes.byref(pft), p, 16, None) == 3         # workspace
+    # route_bwd: ldw < k
+    assert xm._lib_rbwd(p, p, p, p, p, 3, 1, 100, 64, 64, 6, 1.0, 1, p, p, p, 1 << 24, None) == 1

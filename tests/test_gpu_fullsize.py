@@ -18,7 +18,7 @@ import torch
 
 import oracle as orc
 import workloads
-from _helpers import (RTOL, assert_close, by_expert, host, need_gpu, orc_in, pft_invariants, routing_check,
+from _helpers import (buffer_routing, RTOL, assert_close, by_expert, host, need_gpu, orc_in, pft_invariants, routing_check,
                       swiglu_wgrad_scales)
 
 pytestmark = pytest.mark.gpu
@@ -66,26 +66,28 @@ def test_full_size_layer(xm, name):
 
     # PFT
     pft = {k: v.cpu().numpy() for k, v in layer.pft.fields().items()}
-    assert pft["tokens_per_expert"].sum() == wl.T * wl.k
-    np.testing.assert_array_equal(pft["combine_weights"][pft["slot_to_row"]].reshape(wl.T, wl.k),
-                                  layer.topk_w.cpu().numpy())
+    assert pft["tokens_per_expert"].sum() == layer.R
+    bids, bw, bE = buffer_routing(layer, gids, layer.topk_w.cpu().numpy())
+    kb = bids.shape[1]
+    np.testing.assert_array_equal(pft["combine_weights"][pft["slot_to_row"]].reshape(wl.T, kb), bw)
     if not mism.any():
-        ref = orc.build_pft(r["topk_ids"], r["topk_w"].astype(np.float32), wl.E)
+        rids, rw, _ = buffer_routing(layer, r["topk_ids"], r["topk_w"].astype(np.float32))
+        ref = orc.build_pft(rids, rw, bE)
         for key in ("token_ids", "expert_ids", "tokens_per_expert", "expert_offsets"):
             np.testing.assert_array_equal(pft[key], ref[key], err_msg=key)
         # slots of near-tied experts may be ordered differently: compare where the order agrees
         same = (gids == r["topk_ids"]).all(axis=1)
         print(f"[{name}] tokens with near-tied slot order: {int((~same).sum())}", flush=True)
-        np.testing.assert_array_equal(pft["slot_to_row"].reshape(wl.T, wl.k)[same],
-                                      ref["slot_to_row"].reshape(wl.T, wl.k)[same])
-    pft_invariants(gids, layer.topk_w.cpu().numpy(), wl.E, pft)
+        np.testing.assert_array_equal(pft["slot_to_row"].reshape(wl.T, kb)[same],
+                                      ref["slot_to_row"].reshape(wl.T, kb)[same])
+    pft_invariants(bids, bw, bE, pft)
     if wl.zipf_s > 0:
         tpe = pft["tokens_per_expert"]
         assert (tpe == 0).any() and tpe.max() > 10 * tpe.mean()
 
     # dispatch on sampled rows
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(wl.R, size=min(4096, wl.R), replace=False))
+    rows = np.sort(rng.choice(layer.R, size=min(4096, layer.R), replace=False))
     np.testing.assert_array_equal(_sub(layer.xs, rows), _sub(inp["x"], pft["token_ids"][rows]))
 
     # sampled tokens, recomputed by the oracle

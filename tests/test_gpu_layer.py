@@ -12,7 +12,7 @@ import torch
 
 import oracle as orc
 import workloads
-from _helpers import (RTOL, assert_close, assert_wgrad_close, by_expert, host, need_gpu, orc_in, pft_invariants,
+from _helpers import (buffer_routing, RTOL, assert_close, assert_wgrad_close, by_expert, host, need_gpu, orc_in, pft_invariants,
                       router_wgrad_floor, routing_check,
                       swiglu_wgrad_scales)
 
@@ -38,11 +38,12 @@ def _oracle_inputs(inp):
     return out
 
 
-def run_layer(xm, wl, inp, lean=False, overlap=True):
+def run_layer(xm, wl, inp, lean=False, overlap=True, merge=False):
     from padding_free_expert_amd.layer import PaddingFreeMoE
     g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
     weights = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g}
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean, overlap=overlap)
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean, overlap=overlap,
+                           merge_shared=merge)
     layer.forward(g["x"])
     layer.backward(g["dy"])
     torch.cuda.synchronize()
@@ -50,12 +51,16 @@ def run_layer(xm, wl, inp, lean=False, overlap=True):
 
 
 @pytest.mark.parametrize("lean", [False, True], ids=["saved-h13", "lean"])
-@pytest.mark.parametrize("name", NAMES)
-def test_layer_forward_backward(xm, name, lean):
-    """lean=True recomputes H1/H3 in the backward instead of keeping them."""
+@pytest.mark.parametrize("name,merge", [(n, False) for n in NAMES] + [("dsmoe16b", True)],
+                         ids=[n for n in NAMES] + ["dsmoe16b-shared-merged"])
+def test_layer_forward_backward(xm, name, merge, lean):
+    """lean=True recomputes H1/H3 in the backward instead of keeping them;
+    merge=True carries the shared experts as always-routed experts in the
+    routed buffer instead of as their own FFN on a second stream."""
     wl = workloads.small(name)
     inp = workloads.generate(wl, backward=True)
-    layer = run_layer(xm, wl, inp, lean=lean)
+    layer = run_layer(xm, wl, inp, lean=lean, merge=merge)
+    assert layer.merged == (merge and wl.n_shared > 0)
     o = _oracle_inputs(inp)
     mode = 0 if wl.dtype == "f32" else 1
     fwd = orc.layer_forward(o, wl.k, mode, wl.inv_tau, n_shared=wl.n_shared)
@@ -73,18 +78,20 @@ def test_layer_forward_backward(xm, name, lean):
 
     # PFT: integer fields bit-exact whenever the routing agrees
     pft = {k: v.cpu().numpy() for k, v in layer.pft.fields().items()}
-    np.testing.assert_array_equal(pft["combine_weights"][pft["slot_to_row"]].reshape(wl.T, wl.k),
-                                  layer.topk_w.cpu().numpy())
+    bids, bw, bE = buffer_routing(layer, gids, layer.topk_w.cpu().numpy())
+    kb = bids.shape[1]
+    np.testing.assert_array_equal(pft["combine_weights"][pft["slot_to_row"]].reshape(wl.T, kb), bw)
     if not mism.any():
-        ref = orc.build_pft(fwd["route"]["topk_ids"], fwd["route"]["topk_w"].astype(np.float32), wl.E)
+        rids, rw, _ = buffer_routing(layer, fwd["route"]["topk_ids"], fwd["route"]["topk_w"].astype(np.float32))
+        ref = orc.build_pft(rids, rw, bE)
         for key in ("token_ids", "expert_ids", "tokens_per_expert", "expert_offsets"):
             np.testing.assert_array_equal(pft[key], ref[key], err_msg=key)
         # slots of near-tied experts may be ordered differently: compare where the order agrees
         same = (gids == fwd["route"]["topk_ids"]).all(axis=1)
-        np.testing.assert_array_equal(pft["slot_to_row"].reshape(wl.T, wl.k)[same],
-                                      ref["slot_to_row"].reshape(wl.T, wl.k)[same])
+        np.testing.assert_array_equal(pft["slot_to_row"].reshape(wl.T, kb)[same],
+                                      ref["slot_to_row"].reshape(wl.T, kb)[same])
         assert_close(pft["combine_weights"], ref["combine_weights"], 1e-5, "combine_weights")
-    pft_invariants(gids, layer.topk_w.cpu().numpy(), wl.E, pft)
+    pft_invariants(bids, bw, bE, pft)
 
     # dispatch is an exact copy of the rows its own buffer names
     np.testing.assert_array_equal(host(layer.xs), host(inp["x"])[pft["token_ids"]])
@@ -155,13 +162,15 @@ def test_lean_layer_matches_saved_layer_bitwise(xm):
     assert b.saved_bytes() < a.saved_bytes()
 
 
-def test_side_stream_matches_serial_bitwise(xm):
-    """The shared experts on their own stream give bitwise the results of the
-    serial call order (the stream waits carry every dependency)."""
+@pytest.mark.parametrize("merge", [True, False], ids=["shared-merged", "shared-apart"])
+def test_side_stream_matches_serial_bitwise(xm, merge):
+    """The gate backward, the weight gradients and (unmerged) the shared experts
+    on their own streams give bitwise the results of the serial call order
+    (the stream waits carry every dependency)."""
     wl = workloads.small("dsmoe16b")
     inp = workloads.generate(wl, backward=True)
-    a = run_layer(xm, wl, inp, overlap=False)
-    b = run_layer(xm, wl, inp, overlap=True)
+    a = run_layer(xm, wl, inp, overlap=False, merge=merge)
+    b = run_layer(xm, wl, inp, overlap=True, merge=merge)
     assert torch.equal(a.y, b.y)
     for key, ga in a.grads().items():
         assert torch.equal(ga, b.grads()[key]), key

@@ -110,6 +110,26 @@ def test_build_pft_bit_exact(xm, T, E, k, skew):
             np.testing.assert_array_equal(got, ref[key], err_msg=key)
 
 
+@pytest.mark.parametrize("T,E,k,ns,seed", [(300, 16, 6, 2, 0), (1, 8, 2, 1, 1), (4096, 64, 6, 2, 2), (777, 32, 4, 3, 3)])
+def test_build_pft_shared_bit_exact(xm, T, E, k, ns, seed):
+    """Shared experts as always-routed ones: the buffer equals the oracle's
+    buffer of the routing with the n shared experts appended to every token."""
+    ids, w = workloads.random_topk(T, E, k, seed=seed)
+    pft = xm.PFT(T, E + ns, k + ns)
+    ws = torch.empty(max(xm.xmoe_build_pft_workspace_size(T, E + ns, k + ns), 16), dtype=torch.uint8, device="cuda")
+    xm.xmoe_build_pft_shared(ids.cuda(), w.cuda(), E, ns, pft, ws)
+    torch.cuda.synchronize()
+    ids_b = np.concatenate([ids.numpy(), np.tile(np.arange(E, E + ns, dtype=np.int32), (T, 1))], axis=1)
+    w_b = np.concatenate([w.numpy(), np.ones((T, ns), np.float32)], axis=1)
+    ref = orc.build_pft(ids_b, w_b, E + ns)
+    for key, v in pft.fields().items():
+        got = v.cpu().numpy()
+        if key == "combine_weights":
+            np.testing.assert_array_equal(got.view(np.uint32), ref[key].view(np.uint32), err_msg=key)
+        else:
+            np.testing.assert_array_equal(got, ref[key], err_msg=key)
+
+
 def test_build_pft_zero_tokens(xm):
     E, k = 16, 4
     pft = xm.PFT(0, E, k)
@@ -408,6 +428,31 @@ def test_rejects_bad_arguments_without_launching(xm):
     with pytest.raises(xm.XmoeError) as e:
         xm.xmoe_build_pft(ids, w, 8, pft, small_ws)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_route_bwd_strided_dw_and_overwrite(xm, dt):
+    """dtopk_w read as the first k columns of a wider slot buffer, and dx
+    written instead of accumulated: bitwise the dense, accumulate-into-zeros
+    result (and the same dWg)."""
+    T, d, E, k = 333, 256, 16, 4
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(T, d, generator=g).to(dt).cuda()
+    wg = (torch.randn(d, E, generator=g) / d ** 0.5).to(dt).cuda()
+    logits = torch.randn(T, E, generator=g).cuda()
+    ids, _ = workloads.random_topk(T, E, k, seed=8)
+    ids = ids.cuda()
+    wide = torch.randn(T, k + 3, generator=g).cuda()
+    wide[:, k:] = float("nan")        # never read
+    dense = wide[:, :k].contiguous()
+    ws = torch.empty(xm.xmoe_route_bwd_workspace_size(T, d, E, dt), dtype=torch.uint8, device="cuda")
+    dx1, dwg1 = torch.zeros(T, d, dtype=dt, device="cuda"), torch.empty(d, E, device="cuda")
+    xm.xmoe_route_bwd(x, wg, logits, ids, dense, dx1, dwg1, ws, 1.5)
+    dx2 = torch.full((T, d), float("nan"), dtype=dt, device="cuda")
+    dwg2 = torch.empty(d, E, device="cuda")
+    xm.xmoe_route_bwd(x, wg, logits, ids, wide[:, :k], dx2, dwg2, ws, 1.5, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2) and torch.equal(dwg1, dwg2)
 
 
 @pytest.mark.parametrize("T,d,E,k,inv_tau", [(4096, 2048, 64, 6, 1.0), (32768, 4096, 160, 8, 2.0)])
