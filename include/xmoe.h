@@ -299,6 +299,20 @@ xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void 
 xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtype dtype,
                                      const int32_t *expert_offsets, int32_t E, int64_t rows,
                                      int32_t d, int32_t h, void *dw1, void *dw3, void *stream);
+/*
+ * xmoe_expert_ffn_bwd_dw13 with the dispatch gather fused into the loads of
+ * xs (X-MoE article, section 2.1.2: the PFT's token_ids name each row's source
+ * token): dw1[e] = xs_e^T . dH1 and dw3[e] = xs_e^T . dH3 with xs[r] replaced
+ * by x[token_ids[r]], so the backward needs no expert-sorted copy of x.
+ * x [T,d]; token_ids: DEVICE int32 [rows] with values in [0, T) (bf16 reads
+ * outside x return 0, fp32 reads are not checked).  Results are bitwise those
+ * of xmoe_dispatch + xmoe_expert_ffn_bwd_dw13.  Limits as
+ * xmoe_expert_ffn_bwd_dw13, plus T * d * element size < 2^31 bytes.
+ */
+xmoe_status xmoe_expert_ffn_bwd_dw13_gather(const void *x, const int32_t *token_ids, const void *dh13,
+                                            xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
+                                            int64_t T, int64_t rows, int32_t d, int32_t h, void *dw1,
+                                            void *dw3, void *stream);
 xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,
                                     const int32_t *expert_offsets, int32_t E, int64_t rows,
                                     int32_t d, int32_t h, void *dw2, void *stream);

@@ -20,7 +20,7 @@ __all__ = [
     "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_build_pft_shared", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
-    "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13",
+    "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13", "xmoe_expert_ffn_bwd_dw13_gather",
     "xmoe_expert_ffn_bwd_dw2", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
     "xmoe_build_pilots_workspace_size", "xmoe_build_pilots", "xmoe_ep_send_plan", "xmoe_ep_recv_plan_workspace_size",
     "xmoe_ep_recv_plan", "xmoe_scatter_rows",
@@ -78,6 +78,8 @@ _lib_ffn_bwd = _sig("xmoe_expert_ffn_bwd", [_vp, _vp, _vp, _vp, _vp, _vp, _vp, c
 _lib_bwd_dact = _sig("xmoe_expert_ffn_bwd_dact", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
 _lib_bwd_dx = _sig("xmoe_expert_ffn_bwd_dx", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
 _lib_bwd_dw13 = _sig("xmoe_expert_ffn_bwd_dw13", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp])
+_lib_bwd_dw13_g = _sig("xmoe_expert_ffn_bwd_dw13_gather",
+                       [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp])
 _lib_bwd_dw2 = _sig("xmoe_expert_ffn_bwd_dw2", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
 _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp,
                                                _vp, _vp])
@@ -294,6 +296,14 @@ def xmoe_expert_ffn_bwd_dw13(xs, dh13, expert_offsets, dw1, dw3, stream=None):
     E, _, h = dw1.shape
     _check(_lib_bwd_dw13(_ptr(xs), _ptr(dh13), _dt(xs), _ptr(expert_offsets), E, rows, d, h, _ptr(dw1), _ptr(dw3),
                          _stream(stream)), "xmoe_expert_ffn_bwd_dw13")
+
+
+def xmoe_expert_ffn_bwd_dw13_gather(x, token_ids, dh13, expert_offsets, dw1, dw3, stream=None):
+    T, d = x.shape
+    E, _, h = dw1.shape
+    rows = dh13.shape[0]
+    _check(_lib_bwd_dw13_g(_ptr(x), _ptr(token_ids), _ptr(dh13), _dt(x), _ptr(expert_offsets), E, T, rows, d, h,
+                           _ptr(dw1), _ptr(dw3), _stream(stream)), "xmoe_expert_ffn_bwd_dw13_gather")
 
 
 def xmoe_expert_ffn_bwd_dw2(act, dye, expert_offsets, dw2, stream=None):

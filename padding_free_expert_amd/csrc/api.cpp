@@ -387,8 +387,24 @@ xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtyp
     REQUIRE(aligned16(xs) && aligned16(dh13) && aligned16(dw1) && aligned16(dw3), XMOE_ERR_UNSUPPORTED,
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, xs, dh13, expert_offsets, E, rows, d, h, dw1, dw3, S(stream)),
+    return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, xs, nullptr, 0, dh13, expert_offsets, E, rows, d, h, dw1, dw3,
+                                                S(stream)),
                       "xmoe_expert_ffn_bwd_dw13 launch");
+}
+
+xmoe_status xmoe_expert_ffn_bwd_dw13_gather(const void *x, const int32_t *token_ids, const void *dh13,
+                                            xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E, int64_t T,
+                                            int64_t rows, int32_t d, int32_t h, void *dw1, void *dw3, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(dw1 && dw3 && (rows == 0 || dh13), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    TRY(check_gather(x, token_ids, T, rows, d, dtype));
+    REQUIRE(aligned16(dh13) && aligned16(dw1) && aligned16(dw3), XMOE_ERR_UNSUPPORTED,
+            "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, x, token_ids, T, dh13, expert_offsets, E, rows, d, h, dw1, dw3,
+                                                S(stream)),
+                      "xmoe_expert_ffn_bwd_dw13_gather launch");
 }
 
 xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,

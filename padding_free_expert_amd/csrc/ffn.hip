@@ -173,9 +173,11 @@ hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const voi
     return err;
 }
 
-// dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert)
-hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const int32_t *offsets, int E, int64_t rows,
-                               int d, int h, void *dw1, void *dw3, hipStream_t s) {
+// dW1[e] = xs_e^T . dH1_e and dW3[e] = xs_e^T . dH3_e (zeros for an empty expert);
+// with row_map, xs[r] is read as xs[row_map[r]] (xs then has map_rows rows)
+hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *dh13,
+                               const int32_t *offsets, int E, int64_t rows, int d, int h, void *dw1, void *dw3,
+                               hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     const size_t esz = dt == kBF16 ? 2 : 4;
     hipError_t err;
@@ -191,12 +193,19 @@ hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const i
     p.Cx = dw3;
     p.ldc = h;
     p.c_gstride = dh;
+    p.a_map = row_map;  // the gather fused into the A loads: k row r reads xs[row_map[r]]
+    p.a_map_rows = map_rows;
     // short reductions (few rows per expert) leave each tile little work to
     // hide its pipeline fill and epilogue behind: three blocks per compute unit
     // (two-slot rings) overlap more of them
     if (dt != kBF16) return launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
-    err = rows / (E > 0 ? E : 1) < 1024 ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 2, EPI_STORE, bf16_t, 3>(p, s)
-                                        : launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
+    const bool short_k = rows / (E > 0 ? E : 1) < 1024;
+    if (row_map)
+        err = short_k ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 2, EPI_STORE, bf16_t, 3, true>(p, s)
+                      : launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2, true>(p, s);
+    else
+        err = short_k ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 2, EPI_STORE, bf16_t, 3>(p, s)
+                      : launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
     return err;
 }
 
@@ -226,7 +235,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
                           void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s) {
     hipError_t err = launch_ffn_bwd_dact(dt, dye, w2, h13, offsets, E, rows, d, h, dh13, s);
     if (err == hipSuccess) err = launch_ffn_bwd_dx(dt, dh13, w1, w3, offsets, E, rows, d, h, dxs, s);
-    if (err == hipSuccess) err = launch_ffn_bwd_dw13(dt, xs, dh13, offsets, E, rows, d, h, dw1, dw3, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dw13(dt, xs, nullptr, 0, dh13, offsets, E, rows, d, h, dw1, dw3, s);
     if (err == hipSuccess) err = launch_ffn_bwd_dw2(dt, act, dye, offsets, E, rows, d, h, dw2, s);
     return err;
 }

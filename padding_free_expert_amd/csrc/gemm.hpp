@@ -54,6 +54,8 @@ struct GemmArgs {
     // GM_ROWS with a k-contiguous A (bf16 pipelined and fp32 kernels only):
     // when a_map is set, row r of the rows-space reads A0 row a_map[r] (A0 has
     // a_map_rows rows), i.e. the dispatch gather happens in the operand loads.
+    // GM_KSPLIT with an mn-contiguous A (fp32 kernel, or the pipelined kernel's
+    // KMAP variant): k row r reads A0 row a_map[r] the same way.
     const int32_t *a_map;
     int64_t a_map_rows;
     // GM_ROWS split over k (pipelined kernel only): block b works on k range
@@ -398,6 +400,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, int voff, u
                  : "memory");
 }
 
+// One 4-byte-per-lane load into LDS at `lds` (wave-uniform) + 4*lane.
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rs, int voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ int lds_read_i32(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) int *>(static_cast<uintptr_t>(a));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -422,20 +436,30 @@ __device__ __forceinline__ int swz_mn(int k, int cpr) {
 // Per-thread load plan of one operand tile (R mn x BK k), the same for every
 // stage: NW waves x 64 lanes x 16 bytes per instruction, kN instructions per
 // thread; instruction i of wave w fills the tile's 1 KiB block i*NW + w.
-template <int R, int BK, bool KC, int NW>
+template <int R, int BK, bool KC, int NW, bool CMP = false>
 struct DmaPlan {
     static constexpr int kRowBytes = KC ? BK * 2 : R * 2;
     static constexpr int kCpr = kRowBytes / 16;
     static constexpr int kBytes = R * BK * 2;
     static constexpr int kN = kBytes / (NW * 1024);
+    static constexpr int kRpi = 1024 / kRowBytes;  // MN: k rows per instruction
     static_assert(kBytes % (NW * 1024) == 0, "operand tile must be a whole number of block-wide loads");
     static_assert(KC ? (BK == 32 || BK == 64) : (R == 64 || R == 128 || R == 256 || R == 512), "unsupported tile");
-    int base[kN];  // byte offset of this lane's chunk at the stage's first k
-    int lim[kN];   // the chunk is in range iff k0 < lim (INT_MIN: row/column out of range)
+    // CMP (compact, MN with 4+ rows per instruction): the swizzle depends on
+    // k mod 4 only, so every instruction of a lane reads the same columns and
+    // instruction i's row is row 0 + i*NW*kRpi; one base and one limit then
+    // serve all instructions (fewer registers live across the k loop).
+    static_assert(!CMP || (!KC && kRpi % 4 == 0), "compact plans: mn-contiguous, 4+ rows per instruction");
+    static constexpr int kS = CMP ? 1 : kN;
+    static constexpr int kIStep = NW * kRpi;  // CMP: k rows between consecutive instructions
+    int base[kS];  // byte offset of this lane's chunk at the stage's first k
+    int lim[kS];   // the chunk is in range iff k0 < lim (INT_MIN: row/column out of range;
+                   // CMP: instruction i iff k0 < lim - i*kIStep, INT_MIN/2 out of range)
+    int step;      // CMP: bytes between consecutive instructions' rows (kIStep rows)
     // KC: rows r < rmax (r relative to the tile); MN: columns r0 + 8c < rmax
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int r0, int rmax, int kmax) {
 #pragma unroll
-        for (int i = 0; i < kN; ++i) {
+        for (int i = 0; i < kS; ++i) {
             const int o = (i * NW + wave) * 1024 + lane * 16;
             const int row = o / kRowBytes, s = (o % kRowBytes) / 16;
             if constexpr (KC) {
@@ -445,9 +469,10 @@ struct DmaPlan {
             } else {
                 const int c = s ^ swz_mn(row, kCpr);
                 base[i] = static_cast<int>((row * ld + r0 + 8 * c) * 2);
-                lim[i] = r0 + 8 * c < rmax ? kmax - row : INT_MIN;
+                lim[i] = r0 + 8 * c < rmax ? kmax - row : (CMP ? INT_MIN / 2 : INT_MIN);
             }
         }
+        step = static_cast<int>(kIStep * ld * 2);
     }
     // KC rows read through a row map: tile row `row` < rmax is memory row rmap[row]
     __device__ __forceinline__ void init_mapped(int wave, int lane, int64_t ld, const int32_t *rmap, int rmax,
@@ -463,11 +488,26 @@ struct DmaPlan {
             lim[i] = row < rmax ? kmax - 8 * c : INT_MIN;
         }
     }
+    // CMP plan of an MN tile whose k rows are read through a row map: base
+    // keeps the column part only; the row part (map[k] * ld * 2) comes per block
+    __device__ __forceinline__ void init_mn_mapped(int wave, int lane, int r0, int rmax, int kmax) {
+        static_assert(CMP, "k-row maps use the compact plan");
+        init(wave, lane, 0, r0, rmax, kmax);
+    }
     // instruction i of the k block starting at kc (INT_MAX: a block past the end);
     // KC: kadd = 2*k0; MN: the buffer starts at the block's first k row
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int kc, int kadd, uint32_t dst, int wave,
                                           int i) const {
-        lds_dma16(rs, kc < lim[i] ? base[i] + kadd : kOob, dst + (i * NW + wave) * 1024);
+        if constexpr (CMP)
+            lds_dma16(rs, kc < lim[0] - i * kIStep ? base[0] + i * step + kadd : kOob, dst + (i * NW + wave) * 1024);
+        else
+            lds_dma16(rs, kc < lim[i] ? base[i] + kadd : kOob, dst + (i * NW + wave) * 1024);
+    }
+    // CMP, row-mapped: instruction i reads the source row at byte offset roff
+    __device__ __forceinline__ void issue_row(__amdgpu_buffer_rsrc_t rs, int kc, int roff, uint32_t dst, int wave,
+                                              int i) const {
+        static_assert(CMP, "k-row maps use the compact plan");
+        lds_dma16(rs, kc < lim[0] - i * kIStep ? roff + base[0] : kOob, dst + (i * NW + wave) * 1024);
     }
 };
 
@@ -507,7 +547,7 @@ struct FragAddr {
 // the ragged last row tile of an expert costs matrix-core time only for its
 // valid wave rows.
 template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT,
-          int OCC>
+          int OCC, bool KMAP = false>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
 void gemm_dma_kernel(GemmArgs p) {
     constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -515,20 +555,34 @@ void gemm_dma_kernel(GemmArgs p) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile must be a multiple of 32");
-    using PA = DmaPlan<BM, BK, A_KC, NW>;
-    using PB = DmaPlan<BN, BK, B_KC, NW>;
+    // the KMAP kernel keeps its mn-contiguous plans compact (registers for the ids)
+    using PA = DmaPlan<BM, BK, A_KC, NW, KMAP>;
+    using PB = DmaPlan<BN, BK, B_KC, NW, KMAP && !B_KC && (512 / BN) % 4 == 0>;
     constexpr int kABytes = PA::kBytes, kBBytes = PB::kBytes;
     constexpr int kStage = kABytes + NB * kBBytes;
-    constexpr int kL = PA::kN + NB * PB::kN;   // loads per thread per k block
-    static_assert(S >= 2 && kL * (S - 2) <= 63, "vmcnt range");
-    static_assert(S * kStage <= 160 * 1024 / OCC - 64, "OCC blocks per CU must fit the 160 KiB of LDS");
+    constexpr int kL = PA::kN + NB * PB::kN;   // operand loads per thread per k block
+    // KMAP: GM_KSPLIT with an mn-contiguous A whose k rows are read through
+    // p.a_map (row k of the group reads A0 row a_map[base + k]).  Each wave
+    // needs the ids of kIds rows per k block; they reach a ring of kIdQ LDS
+    // regions per wave by one more direct-to-LDS load per block, issued 2S-2
+    // blocks ahead, so that they sit behind the same vector-memory count as
+    // the operand tiles and no scalar or register load enters the loop.
+    static_assert(!KMAP || (!A_KC && EPI == EPI_STORE), "k-row maps: mn-contiguous A, plain store");
+    constexpr int kRpi = PA::kRpi;                        // k rows per A load instruction
+    constexpr int kIds = KMAP ? PA::kN * kRpi : 0;        // ids per wave per k block (= BK / NW)
+    constexpr int kIdQ = 2 * S - 2;
+    constexpr int kIdBytes = KMAP ? kIdQ * NW * 256 : 0;
+    constexpr int kLi = kL + (KMAP ? 1 : 0);              // loads per thread per k block
+    static_assert(kIds <= 64, "one id per lane");
+    static_assert(S >= 2 && kLi * (S - 2) <= 63, "vmcnt range");
+    static_assert(S * kStage + kIdBytes <= 160 * 1024 / OCC - 64, "OCC blocks per CU must fit the 160 KiB of LDS");
     constexpr int KK = BK / 16;
     static_assert(KK == 2 || KK == 4, "BK must be 32 or 64");
     constexpr int NM = NB * TN * TM;                 // products per k step
     constexpr int NR = TM + NB * TN;                 // fragments per k step
     constexpr int DPK = (kL + KK - 2) / (KK - 1);    // loads per k step (all steps but the last)
     constexpr int DPQ = (DPK + NM - 1) / NM;         // loads per product
-    __shared__ __align__(1024) char smem[S * kStage];
+    __shared__ __align__(1024) char smem[S * kStage + kIdBytes];
 
     Tile t;
     // a split over k gives consecutive blocks the parts of one tile
@@ -559,6 +613,8 @@ void gemm_dma_kernel(GemmArgs p) {
     if constexpr (A_KC) {
         if (amap) pa.init_mapped(wave, lane, p.lda, p.a_map + t.base + m0, t.Mg - m0, t.Kg);
         else pa.init(wave, lane, p.lda, 0, t.Mg - m0, t.Kg);
+    } else if constexpr (KMAP) {
+        pa.init_mn_mapped(wave, lane, m0, t.Mg, t.Kg);
     } else {
         pa.init(wave, lane, p.lda, m0, t.Mg, t.Kg);
     }
@@ -581,6 +637,24 @@ void gemm_dma_kernel(GemmArgs p) {
         ra0 = amap ? make_rsrc(p.A0, p.a_map_rows * p.lda * 2) : rs_kc(q.A0, m0, t.Mg, p.lda);
         ra1 = q.A1 ? rs_kc(q.A1, m0, t.Mg, p.lda) : ra0;
     }
+    // KMAP: A's buffer spans the whole source matrix (a_map_rows * lda * 2 <
+    // 2^31 bytes), the ids' buffer the group's map entries
+    const uint32_t idbase = sbase + S * kStage;
+    __amdgpu_buffer_rsrc_t rid = none;
+    int id_row = -1;   // KMAP: the k row (within a block) whose id this lane loads
+    const int lda2 = static_cast<int>(p.lda) * 2;
+    if constexpr (KMAP) {
+        ra0 = make_rsrc(p.A0, p.a_map_rows * p.lda * 2);
+        rid = make_rsrc(p.a_map + t.base, static_cast<int64_t>(t.Kg) * 4);
+        if (lane < kIds) id_row = ((lane / kRpi) * NW + wave) * kRpi + lane % kRpi;
+    }
+    // KMAP: the ids of block st go to region st % kIdQ of this wave (rows past
+    // the group's end, and blocks past the end, load zeros)
+    auto issue_ids = [&](int st) {
+        const int k0 = kstart + st * BK;
+        lds_dma4(rid, st < total && id_row >= 0 ? (k0 + id_row) * 4 : kOob,
+                 idbase + ((st % kIdQ) * NW + wave) * 256);
+    };
     if constexpr (B_KC) {
         rb0 = rs_kc(q.B0, n0, p.N, p.ldb);
         rb1 = q.B1 ? rs_kc(q.B1, n0, p.N, p.ldb) : rb0;
@@ -596,6 +670,7 @@ void gemm_dma_kernel(GemmArgs p) {
     struct StagePlan {
         __amdgpu_buffer_rsrc_t ra, rb, rx;
         int kc, kadd;
+        int arow[KMAP ? PA::kN : 1];  // KMAP: byte offset of this lane's source row, per A instruction
     };
     auto plan_stage = [&](int st) {
         StagePlan sp;
@@ -604,8 +679,17 @@ void gemm_dma_kernel(GemmArgs p) {
         const int k0 = live ? kstart + (st - ph * ktiles) * BK : 0;
         sp.kc = live ? k0 : INT_MAX;
         sp.kadd = 2 * k0;
-        if constexpr (A_KC) sp.ra = ph ? ra1 : ra0;
-        else sp.ra = rs_mn(ph ? q.A1 : q.A0, p.lda, k0);
+        if constexpr (A_KC) {
+            sp.ra = ph ? ra1 : ra0;
+        } else if constexpr (KMAP) {
+            // this wave's ids of block st (landed: see the waits on the ids' loads)
+            sp.ra = ra0;
+            const uint32_t ib = idbase + ((st % kIdQ) * NW + wave) * 256 + 4 * (lane / PA::kCpr);
+#pragma unroll
+            for (int i = 0; i < PA::kN; ++i) sp.arow[i] = lds_read_i32(ib + 4 * kRpi * i) * lda2;
+        } else {
+            sp.ra = rs_mn(ph ? q.A1 : q.A0, p.lda, k0);
+        }
         if constexpr (B_KC) {
             sp.rb = ph ? rb1 : rb0;
             sp.rx = rbx;
@@ -618,7 +702,10 @@ void gemm_dma_kernel(GemmArgs p) {
     // load instruction `part` (0 .. kL-1) of a k block into the slot at `dst`
     auto issue_part = [&](const StagePlan &sp, uint32_t dst, int part) {
         if (part < PA::kN) {
-            pa.issue(sp.ra, sp.kc, A_KC ? sp.kadd : 0, dst, wave, part);
+            if constexpr (KMAP)
+                pa.issue_row(sp.ra, sp.kc, sp.arow[part], dst, wave, part);
+            else
+                pa.issue(sp.ra, sp.kc, A_KC ? sp.kadd : 0, dst, wave, part);
         } else {
             const int pp = part - PA::kN;
             const int b = pp / PB::kN, i = pp % PB::kN;
@@ -662,14 +749,23 @@ void gemm_dma_kernel(GemmArgs p) {
         }
     };
 
-    // prologue: blocks 0 .. S-2 in flight; wait for block 0; its first fragments
+    // prologue: blocks 0 .. S-2 in flight; wait for block 0; its first
+    // fragments.  KMAP: the ids of blocks 0 .. S-2 land first, and block s's
+    // tiles go out behind the ids of block s+S-1, the order the loop keeps
+    // (ids of block st+S-1, then block st's tiles).
+    if constexpr (KMAP) {
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s) issue_ids(s);
+        wait_vmem<0>();
+    }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
+        if constexpr (KMAP) issue_ids(s + S - 1);
         const StagePlan sp = plan_stage(s);
 #pragma unroll
         for (int u = 0; u < kL; ++u) issue_part(sp, sbase + s * kStage, u);
     }
-    wait_vmem<kL * (S - 2)>();
+    wait_vmem<kLi * (S - 2)>();
     __syncthreads();
     // The k loop, instantiated for waves with output (products and fragment
     // reads) and without (loads and barriers only); both meet the same barriers.
@@ -684,6 +780,14 @@ void gemm_dma_kernel(GemmArgs p) {
             const uint32_t sa = sbase + cur * kStage;
             const int nxt = cur + 1 == S ? 0 : cur + 1;
             const uint32_t sf = sbase + (cur == 0 ? S - 1 : cur - 1) * kStage;  // freed by the last barrier
+            // KMAP: block it+2S-2's ids go out before block it+S-1's tiles.  Per
+            // block a thread then issues kLi loads, ids first, so the wait below
+            // (all but the last kLi*(S-2)) also covers the ids of block it+S,
+            // issued just before block it+1's tiles, which the next iteration's
+            // plan reads.  Region (st % kIdQ) is next written by the ids of
+            // block st+2S-2, issued in iteration st, after block st's ids were
+            // read (iteration st-S+1 or the prologue).
+            if constexpr (KMAP) issue_ids(it + 2 * S - 2);
             const StagePlan sp = plan_stage(it + S - 1);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
@@ -691,7 +795,7 @@ void gemm_dma_kernel(GemmArgs p) {
                 uint32_t rs = sa;
                 int rk = kk + 1;
                 if (kk == KK - 1) {
-                    wait_vmem<kL * (S - 2)>();  // this wave's loads of block it+1 have landed
+                    wait_vmem<kLi * (S - 2)>();  // this wave's loads of block it+1 have landed
                     __syncthreads();            // ... everyone's, and all reads of block it are done
                     rs = sbase + nxt * kStage;
                     rk = 0;
@@ -912,11 +1016,12 @@ void gemm_dma_kernel(GemmArgs p) {
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT,
-          int OCC>
+          int OCC, bool KMAP = false>
 inline hipError_t launch_gemm_dma(const GemmArgs &p, hipStream_t stream) {
+    if (KMAP && (p.a_map == nullptr || p.group_mode != GM_KSPLIT)) return hipErrorInvalidValue;
     const int64_t grid = gemm_grid<BM, BN>(p);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WGM, WGN, NB, A_KC, B_KC, S, EPI, OutT, OCC>),
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WGM, WGN, NB, A_KC, B_KC, S, EPI, OutT, OCC, KMAP>),
                        dim3(static_cast<unsigned>(grid)), dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
@@ -955,11 +1060,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
                 const int kk = e / BM, mm = e % BM;
                 const int gm = m0 + mm, gk = k0 + kk;
                 float va = 0.0f;
-                if (gm < t.Mg && gk < t.Kg)
+                if (gm < t.Mg && gk < t.Kg) {
                     if (A_KC && p.a_map && p.group_mode == GM_ROWS)
                         va = static_cast<const float *>(p.A0)[static_cast<int64_t>(p.a_map[t.base + gm]) * p.lda + gk];
+                    else if (!A_KC && p.a_map && p.group_mode == GM_KSPLIT)
+                        va = static_cast<const float *>(p.A0)[static_cast<int64_t>(p.a_map[t.base + gk]) * p.lda + gm];
                     else
                         va = A_KC ? A[static_cast<int64_t>(gm) * p.lda + gk] : A[static_cast<int64_t>(gk) * p.lda + gm];
+                }
                 As[kk][mm] = va;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {

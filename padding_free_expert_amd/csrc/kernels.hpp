@@ -73,8 +73,10 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
                                int64_t rows, int d, int h, void *dh13, hipStream_t s);
 hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
                              int64_t rows, int d, int h, void *dxs, hipStream_t s);
-hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const void *dh13, const int32_t *offsets, int E, int64_t rows,
-                               int d, int h, void *dw1, void *dw3, hipStream_t s);
+// row_map (may be nullptr): k row r of an expert reads xs[row_map[r]] (xs has map_rows rows)
+hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *dh13,
+                               const int32_t *offsets, int E, int64_t rows, int d, int h, void *dw1, void *dw3,
+                               hipStream_t s);
 hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const int32_t *offsets, int E, int64_t rows,
                               int d, int h, void *dw2, hipStream_t s);
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,

@@ -13,8 +13,8 @@ from typing import Dict
 import torch
 
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_shared, xmoe_build_pft_workspace_size, xmoe_combine,
-               xmoe_combine_bwd, xmoe_dispatch, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd,
-               xmoe_expert_ffn_bwd_dact, xmoe_expert_ffn_bwd_dw13, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx,
+               xmoe_combine_bwd, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd,
+               xmoe_expert_ffn_bwd_dact, xmoe_expert_ffn_bwd_dw13_gather, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx,
                xmoe_expert_ffn_gather, xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
                xmoe_route_bwd_workspace_size, xmoe_route_workspace_size)
 
@@ -26,10 +26,10 @@ class PaddingFreeMoE:
     weights s1/s3 [d, n*h_s], s2 [n*h_s, d] (the shared experts side by side),
     logit_bias / select_bias fp32 [E].
 
-    The forward never materialises the expert-sorted copy of x: the gather is
-    fused into the up-projection's operand loads (X-MoE article, section 2.1.2).
-    The backward re-gathers it once, as scratch, for the weight gradient of
-    W1/W3.  lean=True also drops the saved pre-activations H1/H3 and recomputes
+    Neither pass materialises the expert-sorted copy of x: the gather is fused
+    into the operand loads of the up-projection and of the weight gradient of
+    W1/W3 (X-MoE article, section 2.1.2).  lean=True also drops the saved
+    pre-activations H1/H3 and recomputes
     them in the backward (the same kernel, so bitwise the same values): what
     the backward needs from the forward shrinks to act, ye and the routing.
 
@@ -89,8 +89,6 @@ class PaddingFreeMoE:
         self.pft = PFT(T, Ec, kc, dev)
         self.pft_ws = torch.empty(max(xmoe_build_pft_workspace_size(T, Ec, kc), 16), dtype=torch.uint8, device=dev)
         self.route_ws = torch.empty(max(xmoe_route_workspace_size(T, d, E, dt), 16), dtype=torch.uint8, device=dev)
-        # scratch of the backward (re-gathered rows), not kept from the forward
-        self.xs = torch.empty((R, d), dtype=dt, device=dev) if backward else None
         self.act = torch.empty((R, h), dtype=dt, device=dev)
         self.h13 = torch.empty((R, 2 * h), dtype=dt, device=dev) if backward else None
         self.ye = torch.empty((R, d), dtype=dt, device=dev)
@@ -206,19 +204,16 @@ class PaddingFreeMoE:
             mark("recompute_h13")
         off = self.pft.expert_offsets
         ws = self.wside if self.overlap else main
-        # weight gradients: dW2 needs act and dye only; dW1/dW3 need the rows
-        # (re-gathered as scratch) and dH1/dH3
+        # weight gradients: dW2 needs act and dye only; dW1/dW3 need dH1/dH3 and
+        # the token rows, gathered through the PFT inside their loads
         ws.wait_stream(main)
         xmoe_expert_ffn_bwd_dw2(self.act, self.dye, off, self.dW2, stream=ws)
         if ws is main:
             mark("bwd_dw2")
-        xmoe_dispatch(self.x, self.kc, self.pft, self.xs, stream=ws)
-        if ws is main:
-            mark("dispatch")
         xmoe_expert_ffn_bwd_dact(self.dye, self.W2, self.h13, off, self.dh13, stream=main)
         mark("bwd_dact")
         ws.wait_stream(main)
-        xmoe_expert_ffn_bwd_dw13(self.xs, self.dh13, off, self.dW1, self.dW3, stream=ws)
+        xmoe_expert_ffn_bwd_dw13_gather(self.x, self.pft.token_ids, self.dh13, off, self.dW1, self.dW3, stream=ws)
         if ws is main:
             mark("bwd_dw13")
         xmoe_expert_ffn_bwd_dx(self.dh13, self.W1, self.W3, off, self.dxs, stream=main)

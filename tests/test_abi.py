@@ -100,3 +100,19 @@ def test_shared_buffer_and_route_bwd_reject_on_host(xm):
     assert xm._lib_pft_sh(p, p, 100000, 64, 6, 2, ctypes.byref(pft), p, 16, None) == 3         # workspace
     # route_bwd: ldw < k
     assert xm._lib_rbwd(p, p, p, p, p, 3, 1, 100, 64, 64, 6, 1.0, 1, p, p, p, 1 << 24, None) == 1
+
+
+def test_gathered_wgrad_rejects_on_host(xm):
+    p = ctypes.c_void_p(16)  # never dereferenced
+    f = xm._lib_bwd_dw13_g
+    # x [T, d] of 2^31 bytes or more cannot be gathered through one buffer
+    assert f(p, p, p, 1, p, 4, 1 << 17, 100, 8192, 64, p, p, None) == 2
+    # NULL x or token_ids with rows to gather; NULL dh13
+    assert f(None, p, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
+    assert f(p, None, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
+    assert f(p, p, None, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
+    # T < 1, h not a multiple of 8, misaligned x
+    assert f(p, p, p, 1, p, 4, 0, 100, 64, 64, p, p, None) == 1
+    assert f(p, p, p, 1, p, 4, 100, 100, 64, 12, p, p, None) == 2
+    assert f(ctypes.c_void_p(18), p, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 2
+    assert xm._lib_last_error() != b""

@@ -4,7 +4,7 @@ benchmark times (the whole layer through the C ABI).
 The oracle cannot redo a full-size layer in seconds, so it checks:
   * routing of every token (exact where unambiguous, valid where near-tied);
   * the Padding-Free Token buffer bit for bit (when the routing agrees);
-  * the dispatch copy on sampled rows;
+  * the dispatch copy of the layer's buffer on sampled rows;
   * forward output, input gradient and routing-weight gradient of sampled
     tokens, recomputed token by token;
   * weight gradients: sampled columns of the busiest expert, the whole gradient
@@ -85,10 +85,15 @@ def test_full_size_layer(xm, name):
         tpe = pft["tokens_per_expert"]
         assert (tpe == 0).any() and tpe.max() > 10 * tpe.mean()
 
-    # dispatch on sampled rows
+    # the dispatch copy over the layer's buffer (the layer itself gathers inside
+    # its products), on sampled rows
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(layer.R, size=min(4096, layer.R), replace=False))
-    np.testing.assert_array_equal(_sub(layer.xs, rows), _sub(inp["x"], pft["token_ids"][rows]))
+    xs = torch.empty((layer.R, wl.d), dtype=layer.x.dtype, device="cuda")
+    xm.xmoe_dispatch(layer.x, layer.kc, layer.pft, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_sub(xs, rows), _sub(inp["x"], pft["token_ids"][rows]))
+    del xs
 
     # sampled tokens, recomputed by the oracle
     ok = np.nonzero(~mism)[0]

@@ -325,6 +325,69 @@ def test_expert_ffn_gather(xm, dtype, T, d, h, E, k, skew):
     assert torch.equal(act3, act)
 
 
+# the gathered weight gradient: ragged and empty experts, d and h off the
+# 128-wide tiles, and more than 1024 rows per expert (the three-slot ring)
+DW13_GATHER_CASES = GATHER_CASES + [
+    ("bf16", 2600, 192, 136, 4, 2, 0.5),
+    ("bf16", 1100, 256, 128, 1, 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("dtype,T,d,h,E,k,skew", DW13_GATHER_CASES)
+def test_expert_ffn_bwd_dw13_gather(xm, dtype, T, d, h, E, k, skew):
+    """dW1/dW3 with the dispatch gather fused into the loads of x: against the
+    oracle's expert backward over the same token-to-row map, and bitwise
+    against the same product over the materialised rows x[token_ids]."""
+    ids, w = workloads.random_topk(T, E, k, seed=T + 3 * d, skew=skew)
+    ref_pft = orc.build_pft(ids.numpy(), w.numpy(), E)
+    tok, off = ref_pft["token_ids"], ref_pft["expert_offsets"]
+    R = T * k
+    row_expert = np.repeat(np.arange(E, dtype=np.int32), np.diff(off))
+    x = workloads.random_rows(T, d, dtype, seed=T + 11)
+    dye = workloads.random_rows(R, d, dtype, seed=T + 12)
+    g = torch.Generator().manual_seed(T + h)
+    tdt = DT[dtype]
+    w1 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w3 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w2 = (torch.randn((E, h, d), generator=g) / h ** 0.5).to(tdt)
+    c = lambda t: t.cuda()
+    tok_d, off_d = torch.from_numpy(tok).cuda(), torch.from_numpy(off).cuda()
+    act = torch.empty((R, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((R, 2 * h), dtype=tdt, device="cuda")
+    ye = torch.empty((R, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_gather(c(x), tok_d, c(w1), c(w3), c(w2), off_d, act, ye, h13=h13)
+    dh13 = torch.empty((R, 2 * h), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_bwd_dact(c(dye), c(w2), h13, off_d, dh13)
+    dw1 = torch.full((E, d, h), float("nan"), dtype=tdt, device="cuda")   # must be fully overwritten
+    dw3 = torch.full((E, d, h), float("nan"), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_bwd_dw13_gather(c(x), tok_d, dh13, off_d, dw1, dw3)
+    # the materialised path: same products on the same values, so bitwise
+    xs = c(x)[tok_d.long()].contiguous()
+    dw1m, dw3m = torch.empty_like(dw1), torch.empty_like(dw3)
+    xm.xmoe_expert_ffn_bwd_dw13(xs, dh13, off_d, dw1m, dw3m)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw1m) and torch.equal(dw3, dw3m)
+    # the oracle over the token-to-row map
+    X = host(x)
+    ref = orc.ffn_bwd(orc_in(x), row_expert, orc_in(w1), orc_in(w3), orc_in(w2), orc_in(dye), row_token=tok,
+                      want_dh=True)
+    fwd = orc.ffn(orc_in(x), row_expert, orc_in(w1), orc_in(w3), orc_in(w2), row_token=tok, want_hidden=True)
+    Xr, G = X[tok], host(dye)
+    scales = {}
+
+    def floors(e):
+        if e not in scales:
+            sl = slice(off[e], off[e + 1])
+            scales[e] = swiglu_wgrad_scales(Xr[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl],
+                                            G[sl], host(w2[e]))
+        return scales[e]
+
+    rows = lambda e: off[e + 1] - off[e]
+    rt = RTOL[dtype]
+    assert_wgrad_close(host(dw1), ref["dw1"], rows, lambda e: floors(e)[0], rt, "dw1")
+    assert_wgrad_close(host(dw3), ref["dw3"], rows, lambda e: floors(e)[1], rt, "dw3")
+
+
 @pytest.mark.parametrize("dtype,rows,d,h,E,empty", FFN_CASES)
 def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
     off, xs, w1, w3, w2, re_ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=rows + 2 * d)
