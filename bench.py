@@ -5,7 +5,9 @@ Workload (default): the DeepSeek-MoE-16B-like layer -- 4096 tokens, d = 2048,
 of hidden 1408, bf16 with fp32 accumulation, Gaussian synthetic inputs.  One
 step is the whole hot path: route, PFT build, dispatch, routed and shared
 expert FFN, combine, and the backward of each (combine, experts, dispatch,
-router).  Inputs are resident in HBM before the timed region.
+router).  Inputs are resident in HBM before the timed region.  --workload
+picks another shape; one whose configuration is a forward pass only (the
+DeepSeek-V3 shape) times the forward alone and counts its flops alone.
 
 Prints one JSON line: useful TFLOPS (router + routed + shared expert GEMMs on
 unpadded rows; backward GEMMs count twice the forward), tokens/s, the roofline
@@ -108,14 +110,17 @@ def main():
     inp = workloads.generate(wl, device="cuda", backward=True)
     weights = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias")
                if k in inp}
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=args.lean,
+    # a step is the passes the workload names: forward and backward, or (the
+    # DeepSeek-V3 shape) the forward alone
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=wl.backward, lean=args.lean,
                            overlap=not args.no_overlap, merge_shared=args.merge_shared)
     x, dy = inp["x"], inp["dy"]
     stream = torch.cuda.current_stream()
 
     def step(hook=None):
         layer.forward(x, hook=hook)
-        layer.backward(dy, hook=hook)
+        if wl.backward:
+            layer.backward(dy, hook=hook)
 
     for _ in range(args.warmup):
         step()
@@ -189,7 +194,7 @@ def main():
     up_launches = [(lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, layer.W1, layer.W3,
                                                         layer.pft.expert_offsets, layer.act, layer.h13),
                     4.0 * R * d * h)]
-    up_bytes = [2.0 * (R * d + 2 * layer.Ec * d * h + R * h + R * 2 * h)]
+    up_bytes = [2.0 * (R * d + 2 * layer.Ec * d * h + R * h + (R * 2 * h if layer.h13 is not None else 0))]
     if layer.side_shared:
         hs = layer.hs
         up_launches.append((lambda: xm.xmoe_expert_ffn_up(x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0),
@@ -227,8 +232,10 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "h": wl.h, "k": wl.k,
-                      "n_shared": wl.n_shared, "h_shared": wl.h_shared, "passes": "fwd+bwd",
-                      "h13": "recomputed" if args.lean else "saved",
+                      "n_shared": wl.n_shared, "h_shared": wl.h_shared,
+                      "passes": "fwd+bwd" if wl.backward else "fwd",
+                      "h13": ("not kept (forward only)" if not wl.backward else
+                              "recomputed" if args.lean else "saved"),
                       "shared_experts": ("merged as always-routed experts" if layer.merged else
                                          "side stream" if layer.side_shared and layer.overlap else
                                          "in order" if layer.shared else "none")},
@@ -338,22 +345,24 @@ def cpu_baseline(wl, inp, sample_tokens, layer):
     o["dy"] = o["dy"][:n]
     t0 = time.perf_counter()
     fwd = orc.layer_forward(o, wl.k, 1, wl.inv_tau, n_shared=wl.n_shared)
-    bwd = orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared)
+    bwd = orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared) if wl.backward else None
     dt = time.perf_counter() - t0
     sub = wl.__class__(**{**wl.__dict__, "T": n})
     fl = sub.useful_flops()["total"]
+    what = "full forward+backward incl. all weight gradients" if wl.backward else "full forward"
     base = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS", "cores": orc.get_threads(), "kind": "oracle",
-            "sample": f"{n} of {wl.T} tokens, full forward+backward incl. all weight gradients",
+            "sample": f"{n} of {wl.T} tokens, {what}",
             "seconds": round(dt, 2), "tokens_per_s": round(n / dt, 2)}
     ok = (layer.topk_ids[:n].cpu().numpy() == fwd["route"]["topk_ids"]).all(axis=1)
 
     def rel(g, r):
         g = g[:n].detach().cpu().to(torch.float64).numpy()[ok]
         return float(np.linalg.norm(g - r[ok]) / max(np.linalg.norm(r[ok]), 1e-300))
-    ry, rdx = rel(layer.y, fwd["y"]), rel(layer.dx, bwd["dx"])
+    ry = rel(layer.y, fwd["y"])
+    rdx = rel(layer.dx, bwd["dx"]) if wl.backward else None
     tol = 2e-2
     parity = {"tokens": n, "tokens_compared": int(ok.sum()), "y_rel_err": ry, "dx_rel_err": rdx, "rtol": tol,
-              "pass": bool(ry <= tol and rdx <= tol), "against": "oracle (fp64) on the same inputs"}
+              "pass": bool(ry <= tol and (rdx is None or rdx <= tol)), "against": "oracle (fp64) on the same inputs"}
     return base, parity
 
 

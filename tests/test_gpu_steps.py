@@ -282,6 +282,7 @@ GATHER_CASES = [
     ("bf16", 300, 256, 200, 16, 6, 1.5),   # skewed: some experts empty
     ("bf16", 517, 328, 264, 7, 3, 0.7),    # d and h off every tile multiple
     ("bf16", 129, 128, 128, 1, 1, 0.0),
+    ("bf16", 400, 192, 512, 8, 4, 0.8),    # h a multiple of 256 below 1024 rows per expert
 ]
 
 
