@@ -105,8 +105,11 @@ hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t
     // below 1024 rows per expert, h a multiple of 256: 256 columns of W1 and of
     // W3 per block (eight waves of 64 x 64 x 2) share each row tile twice as
     // long; 7% faster at 256 rows per expert, h = 2048, d = 7168.  With h =
-    // 1408 the last such tile is half empty and the 128-column tile wins.
-    if (h % 256 == 0) return launch_gemm_dma<128, 256, 32, 2, 4, 2, true, false, 3, EPI_SWIGLU, bf16_t, 1>(p, s);
+    // 1408 the last such tile is half empty, and a single dense group (4096
+    // rows, h = 2816, whose large-tile grid is too small) runs 12% slower: both
+    // keep the 128-column tile.
+    if (h % 256 == 0 && rows / (E > 0 ? E : 1) < 1024)
+        return launch_gemm_dma<128, 256, 32, 2, 4, 2, true, false, 3, EPI_SWIGLU, bf16_t, 1>(p, s);
     return launch_gemm_dma<128, 128, 32, 2, 2, 2, true, false, 3, EPI_SWIGLU, bf16_t, 2>(p, s);
 }
 
