@@ -389,6 +389,40 @@ def test_expert_ffn_bwd_dw13_gather(xm, dtype, T, d, h, E, k, skew):
     assert_wgrad_close(host(dw3), ref["dw3"], rows, lambda e: floors(e)[1], rt, "dw3")
 
 
+def test_gathered_reads_outside_x_are_zero(xm):
+    """bf16 gathers read x through a bounds-checked buffer: a token id past T
+    or negative reads a zero row, in the up-projection and in dW1/dW3 alike
+    (bitwise the products over x[token_ids] with those rows zeroed)."""
+    T, d, h, E, k = 200, 256, 128, 4, 2
+    ids, w = workloads.random_topk(T, E, k, seed=5)
+    ref_pft = orc.build_pft(ids.numpy(), w.numpy(), E)
+    tok = ref_pft["token_ids"].copy()
+    R = T * k
+    bad = np.arange(0, R, 17)
+    tok[bad] = np.resize(np.array([T, T + 1000, -1, -7], np.int32), bad.size)
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn((T, d), generator=g).to(bf).cuda()
+    w1 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(bf).cuda()
+    w3 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(bf).cuda()
+    dh13 = torch.randn((R, 2 * h), generator=g).to(bf).cuda()
+    tok_d, off_d = torch.from_numpy(tok).cuda(), torch.from_numpy(ref_pft["expert_offsets"]).cuda()
+    act, h13 = torch.empty((R, h), dtype=bf, device="cuda"), torch.empty((R, 2 * h), dtype=bf, device="cuda")
+    dw1, dw3 = torch.empty((E, d, h), dtype=bf, device="cuda"), torch.empty((E, d, h), dtype=bf, device="cuda")
+    xm.xmoe_expert_ffn_up_gather(x, tok_d, w1, w3, off_d, act, h13)
+    xm.xmoe_expert_ffn_bwd_dw13_gather(x, tok_d, dh13, off_d, dw1, dw3)
+    ok = (tok_d >= 0) & (tok_d < T)
+    xs = torch.where(ok[:, None], x[tok_d.clamp(0, T - 1).long()], torch.zeros((), dtype=bf, device="cuda"))
+    act2, h132 = torch.empty_like(act), torch.empty_like(h13)
+    dw1m, dw3m = torch.empty_like(dw1), torch.empty_like(dw3)
+    xm.xmoe_expert_ffn_up(xs.contiguous(), w1, w3, off_d, act2, h132)
+    xm.xmoe_expert_ffn_bwd_dw13(xs.contiguous(), dh13, off_d, dw1m, dw3m)
+    torch.cuda.synchronize()
+    assert torch.equal(act, act2) and torch.equal(h13, h132)
+    assert torch.equal(dw1, dw1m) and torch.equal(dw3, dw3m)
+    assert (h13[torch.from_numpy(bad).cuda()] == 0).all()
+
+
 @pytest.mark.parametrize("dtype,rows,d,h,E,empty", FFN_CASES)
 def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
     off, xs, w1, w3, w2, re_ = _ffn_inputs(dtype, rows, d, h, E, empty, seed=rows + 2 * d)
