@@ -25,8 +25,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd useful TFLOPS + tokens/s on 1 MI355X (DeepSeek-MoE shape)"
 # HBM bytes per launch of the up-projection from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# runs, recorded with a hash of the kernel sources they were taken on
-COUNTERS = os.path.join(ROOT, "profiles", "up_projection_dsmoe16b_counters.json")
+# runs, per workload, recorded with a hash of the kernel sources they were taken on
+COUNTERS = os.path.join(ROOT, "profiles", "up_projection_counters.json")
 KERNEL_SOURCES = ["common.hpp", "gemm.hpp", "ffn.hip"]
 
 
@@ -39,8 +39,9 @@ def kernel_sources_sha1() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """Counter-measured bytes per launch, or None when the kernel changed since."""
+def recorded_traffic(workload: str):
+    """Counter-measured bytes per launch on this workload, or None when the
+    counters were taken on another workload or the kernel changed since."""
     try:
         with open(COUNTERS) as fh:
             rec = json.load(fh)
@@ -48,7 +49,19 @@ def recorded_traffic():
         return None
     if rec.get("kernel_sources_sha1") != kernel_sources_sha1():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
+
+
+def up_tile(rows: int, E: int, h: int) -> str:
+    """The up-projection tile the library picks for a launch (the selection in
+    launch_ffn_up, csrc/ffn.hip, repeated here only to name the kernel)."""
+    per = rows // max(E, 1)
+    large_grid = (rows // 256 + E) * ((h + 127) // 128) >= 512
+    if per >= 1024 and large_grid:
+        return "gemm_dma_kernel<256,128,32,4,2,2,...,EPI_SWIGLU> (8 waves, 1 block/CU)"
+    if h % 256 == 0 and per < 1024:
+        return "gemm_dma_kernel<128,256,32,2,4,2,...,EPI_SWIGLU> (8 waves, 1 block/CU)"
+    return "gemm_dma_kernel<128,128,32,2,2,2,...,EPI_SWIGLU> (4 waves, 2 blocks/CU)"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
@@ -70,6 +83,10 @@ def parse():
                     help="tokens in the oracle's timed sample (0: pick for ~10-30 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale hardware byte counters)")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="run the warm-up and timed steps only (no cache-flushed steps, per-call breakdown, "
+                         "isolated launches, EP/RBD kernels or CPU baseline), so that a profiler's per-kernel "
+                         "averages cover exactly the steps whose launches the roofline times")
     return ap.parse_args()
 
 
@@ -117,8 +134,8 @@ def main():
     x, dy = inp["x"], inp["dy"]
     stream = torch.cuda.current_stream()
 
-    def step(hook=None):
-        layer.forward(x, hook=hook)
+    def step(hook=None, probe=None):
+        layer.forward(x, hook=hook, probe=probe)
         if wl.backward:
             layer.backward(dy, hook=hook)
 
@@ -127,104 +144,127 @@ def main():
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # events right before and after each up-projection launch of the timed
+    # steps, on the stream it is launched on (routed: the main stream; shared
+    # experts: their side stream)
+    up_ev = {"up": [], "shared_up": []}
+    up_pool = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps)]
+
+    def probe(name, s):
+        e = up_pool.pop()
+        e.record(s)
+        if name.endswith("_end"):
+            up_ev[name[:-4]][-1].append(e)
+        else:
+            up_ev[name].append([e])
+
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step()
+        step(probe=probe)
         marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     per_step = [ev0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
+    up_ms = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in up_ev.items() if v}
 
-    # the same steps with the 256 MB Infinity Cache flushed before each one (a
-    # 1 GiB scratch write outside the step's events), so no input is served
-    # from the last step's cache contents
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    flushed = []
-    for _ in range(min(args.steps, 10)):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        flushed.append(a.elapsed_time(b))
-    del flush
     ms = max(gpu_ms, wall * 1e3 / args.steps)
     flops = wl.useful_flops()
     tflops = flops["total"] / (ms * 1e-3) / 1e12
     tok_s = wl.T / (ms * 1e-3)
 
-    # per-call breakdown: events between library calls, averaged over a few steps
-    names, evs = [], []
+    flushed, breakdown = [], {}
+    if not args.timed_only:
+        # the same steps with the 256 MB Infinity Cache flushed before each one
+        # (a 1 GiB scratch write outside the step's events), so no input is
+        # served from the last step's cache contents
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for _ in range(min(args.steps, 10)):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            flushed.append(a.elapsed_time(b))
+        del flush
 
-    def hook(name):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        names.append(name)
-        evs.append(e)
+        # per-call breakdown: events between library calls, averaged over a few
+        # steps (serially: with the shared experts on their side stream the gaps
+        # between main-stream events would not be per-call times)
+        names, evs = [], []
 
-    # (serially: with the shared experts on their side stream the gaps between
-    # main-stream events would not be per-call times)
-    reps = 5
-    breakdown = {}
-    overlap = layer.overlap
-    layer.overlap = False
-    for _ in range(reps):
-        names.clear()
-        evs.clear()
-        start = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        step(hook)
-        torch.cuda.synchronize()
-        prev = start
-        for n, e in zip(names, evs):
-            breakdown[n] = breakdown.get(n, 0.0) + prev.elapsed_time(e) / reps
-            prev = e
-    layer.overlap = overlap
+        def hook(name):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            names.append(name)
+            evs.append(e)
 
-    # roofline of the dominant kernel: the up-projection (W1|W3 + SwiGLU), launched
-    # once for the routed experts (rows gathered from x through the PFT's
-    # token_ids) and once for the shared experts per step
-    # (with the shared experts merged into the buffer: one launch over the
-    # routed and shared experts together)
+        reps = 5
+        overlap = layer.overlap
+        layer.overlap = False
+        for _ in range(reps):
+            names.clear()
+            evs.clear()
+            start = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            step(hook)
+            torch.cuda.synchronize()
+            prev = start
+            for n, e in zip(names, evs):
+                breakdown[n] = breakdown.get(n, 0.0) + prev.elapsed_time(e) / reps
+                prev = e
+        layer.overlap = overlap
+
+    # roofline of the dominant kernel: the up-projection (W1|W3 + SwiGLU),
+    # launched once for the routed experts (rows gathered from x through the
+    # PFT's token_ids) and, with shared experts beside them, once for those per
+    # step.  Its durations are the timed steps' own launches (events around
+    # each launch on its stream, above), so they include whatever the other
+    # stream runs at the same time, as a profiler's kernel durations do.
     R, d, h = layer.R, wl.d, wl.h
-    up_launches = [(lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, layer.W1, layer.W3,
-                                                        layer.pft.expert_offsets, layer.act, layer.h13),
-                    4.0 * R * d * h)]
-    up_bytes = [2.0 * (R * d + 2 * layer.Ec * d * h + R * h + (R * 2 * h if layer.h13 is not None else 0))]
+    launches = [("up", 4.0 * R * d * h,
+                 2.0 * (R * d + 2 * layer.Ec * d * h + R * h + (R * 2 * h if layer.h13 is not None else 0)))]
     if layer.side_shared:
         hs = layer.hs
-        up_launches.append((lambda: xm.xmoe_expert_ffn_up(x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0),
-                                                          layer.sh_off, layer.sh_act, layer.sh_h13),
-                            4.0 * wl.T * d * hs))
-        up_bytes.append(2.0 * (wl.T * d + 2 * d * hs + wl.T * hs + wl.T * 2 * hs))
-    n_rep = 20
-    tot_ms, tot_flop, per = 0.0, 0.0, []
-    for (launch, fl) in up_launches:
-        for _ in range(3):
-            launch()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n_rep):
-            launch()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / n_rep
-        per.append({"flop": fl, "avg_ms": t, "tflops": fl / (t * 1e-3) / 1e12})
+        launches.append(("shared_up", 4.0 * wl.T * d * hs, 2.0 * (wl.T * d + 2 * d * hs + wl.T * hs
+                                                                 + (wl.T * 2 * hs if layer.sh_h13 is not None else 0))))
+    per, tot_ms, tot_flop, tot_bytes = [], 0.0, 0.0, 0.0
+    for name, fl, by in launches:
+        t = up_ms[name]
+        per.append({"launch": name, "flop": fl, "avg_ms": round(t, 5), "tflops": round(fl / (t * 1e-3) / 1e12, 2)})
         tot_ms += t
         tot_flop += fl
+        tot_bytes += by
+    if not args.timed_only:
+        # the same launches alone, back to back (no other stream running)
+        iso = {"up": lambda: xm.xmoe_expert_ffn_up_gather(x, layer.pft.token_ids, layer.W1, layer.W3,
+                                                         layer.pft.expert_offsets, layer.act, layer.h13),
+               "shared_up": lambda: xm.xmoe_expert_ffn_up(x, weights["s1"].unsqueeze(0), weights["s3"].unsqueeze(0),
+                                                          layer.sh_off, layer.sh_act, layer.sh_h13)}
+        for p in per:
+            launch = iso[p["launch"]]
+            for _ in range(3):
+                launch()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            p["isolated_avg_ms"] = round(e0.elapsed_time(e1) / 20, 5)
     achieved = tot_flop / (tot_ms * 1e-3) / 1e12
     # the same launches against HBM: each operand read once (the gathered rows,
     # the weights) and each output written once (act, H1|H3)
-    hbm_gbps = sum(up_bytes) / (tot_ms * 1e-3) / 1e9
-    roofline = {"kernel": "gemm_dma_kernel<128,128,32,2,2,2,...,EPI_SWIGLU> (expert up-projection, DeepSeek-MoE-16B tile)",
+    hbm_gbps = tot_bytes / (tot_ms * 1e-3) / 1e9
+    roofline = {"kernel": "expert up-projection, " + up_tile(R, layer.Ec, h),
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
-                "launches_per_step": per, "avg_launch_ms": tot_ms / len(up_launches),
-                "hbm": {"algorithmic_bytes_per_launch": round(sum(up_bytes) / len(up_bytes)),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(wl.name),
+                "launches_per_step": per, "avg_launch_ms": round(tot_ms / len(launches), 5),
+                "timed_steps": args.steps,
+                "hbm": {"algorithmic_bytes_per_launch": round(tot_bytes / len(launches)),
                         "achieved_GBps": round(hbm_gbps, 1), "peak_GBps": 8000.0,
                         "frac": round(hbm_gbps / 8000.0, 4)}}
 
@@ -240,13 +280,16 @@ def main():
                                          "side stream" if layer.side_shared and layer.overlap else
                                          "in order" if layer.shared else "none")},
            "tokens_per_s": round(tok_s, 1), "gpu_ms_per_step": round(gpu_ms, 4),
-           "step_ms": pctl(per_step), "step_ms_cache_flushed": pctl(flushed),
+           "step_ms": pctl(per_step),
            "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
            "useful_gflop_per_step": round(flops["total"] / 1e9, 2),
            "saved_activation_mb": round(layer.saved_bytes() / 1e6, 1),
-           "breakdown_ms_serial": {k: round(v, 4) for k, v in breakdown.items()},
            "roofline": roofline}
-
+    if args.timed_only:
+        print(json.dumps(out), flush=True)
+        return
+    out["step_ms_cache_flushed"] = pctl(flushed)
+    out["breakdown_ms_serial"] = {k: round(v, 4) for k, v in breakdown.items()}
     out["ep_rbd"] = ep_rbd(xm, wl, layer, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(wl, inp, args.cpu_sample_tokens, layer)

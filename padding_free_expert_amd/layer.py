@@ -13,9 +13,9 @@ from typing import Dict
 import torch
 
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_shared, xmoe_build_pft_workspace_size, xmoe_combine,
-               xmoe_combine_bwd, xmoe_dispatch_bwd, xmoe_expert_ffn, xmoe_expert_ffn_bwd,
+               xmoe_combine_bwd, xmoe_dispatch_bwd, xmoe_expert_ffn_bwd,
                xmoe_expert_ffn_bwd_dact, xmoe_expert_ffn_bwd_dw13_gather, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx,
-               xmoe_expert_ffn_gather, xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
+               xmoe_expert_ffn_down, xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
                xmoe_route_bwd_workspace_size, xmoe_route_workspace_size)
 
 
@@ -132,17 +132,24 @@ class PaddingFreeMoE:
         side = self.side if (self.side_shared and self.overlap) else main
         return main, side
 
-    def forward(self, x: torch.Tensor, stream=None, hook=None) -> torch.Tensor:
-        """hook(name), if given, is called after each library call is enqueued."""
+    def forward(self, x: torch.Tensor, stream=None, hook=None, probe=None) -> torch.Tensor:
+        """hook(name), if given, is called after each library call is enqueued.
+        probe(name, stream), if given, is called right before and right after
+        each up-projection launch ("up" / "up_end" for the routed experts,
+        "shared_up" / "shared_up_end" for the shared ones) with the stream the
+        launch goes to, e.g. to record events around it."""
         w = self.w
         mark = hook or (lambda name: None)
+        around = probe or (lambda name, s: None)
         main, side = self._streams(stream)
         keep = self.backward_enabled and not self.lean
         if self.side_shared:
             side.wait_stream(main)
             s1, s3, s2 = self._shared_w()
-            xmoe_expert_ffn(x, s1, s3, s2, self.sh_off, self.sh_act, self.sh_y,
-                            h13=self.sh_h13 if keep else None, stream=side)
+            around("shared_up", side)
+            xmoe_expert_ffn_up(x, s1, s3, self.sh_off, self.sh_act, h13=self.sh_h13 if keep else None, stream=side)
+            around("shared_up_end", side)
+            xmoe_expert_ffn_down(self.sh_act, s2, self.sh_off, self.sh_y, stream=side)
             if side is main:
                 mark("shared_ffn")
         xmoe_route(x, w["wg"], self.k, self.topk_ids, self.topk_w, self.logits, self.inv_tau,
@@ -153,8 +160,11 @@ class PaddingFreeMoE:
         else:
             xmoe_build_pft(self.topk_ids, self.topk_w, self.E, self.pft, self.pft_ws, stream=main)
         mark("build_pft")
-        xmoe_expert_ffn_gather(x, self.pft.token_ids, self.W1, self.W3, self.W2, self.pft.expert_offsets,
-                               self.act, self.ye, h13=self.h13 if keep else None, stream=main)
+        around("up", main)
+        xmoe_expert_ffn_up_gather(x, self.pft.token_ids, self.W1, self.W3, self.pft.expert_offsets, self.act,
+                                  h13=self.h13 if keep else None, stream=main)
+        around("up_end", main)
+        xmoe_expert_ffn_down(self.act, self.W2, self.pft.expert_offsets, self.ye, stream=main)
         mark("expert_ffn")
         y_add = None
         if self.side_shared:
