@@ -26,60 +26,110 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// When `part` is set, the logits are first formed from nparts fp32 partial
-// sums of z (a split of the d reduction, summed in part order), then scaled and
-// biased with one IEEE operation each and written to `logits`.
-template <int Q>
+// LT lanes per token (8, 16 or 32), 64 / LT tokens per wavefront; lane r of a
+// token holds the QQ consecutive experts r*QQ .. r*QQ+QQ-1, read as 16-byte
+// vectors when E is a multiple of 4 (QQ always is).  When `part` is set, the
+// logits are first formed from nparts fp32 partial sums of z (a split of the
+// d reduction, summed in part order), then scaled and biased with one IEEE
+// operation each and written to `logits`.  The softmax and the top-k (k
+// rounds of an arg-max under the order (sel desc, index asc)) reduce over the
+// token's LT lanes only: log2(LT) butterfly steps per round instead of six.
+template <int LT, int QQ>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ logits, const float *__restrict__ part,
                                                            int nparts, int64_t part_stride, float scale,
                                                            const float *__restrict__ lbias,
                                                            const float *__restrict__ sbias, int64_t T, int E, int k,
                                                            int32_t *__restrict__ ids, float *__restrict__ w) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (t >= T) return;
+    static_assert(LT == 8 || LT == 16 || LT == 32, "lanes per token");
+    static_assert(QQ % 4 == 0 && QQ <= 32, "whole 16-byte vectors; one bit per value in the taken mask");
+    constexpr int TPW = 64 / LT;
     const int lane = threadIdx.x & 63;
-    float s[Q], sel[Q];
+    const int r = lane % LT;
+    const int e0 = r * QQ;
+    const int64_t t = (static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * TPW + lane / LT;
+    const bool live = t < T;  // every lane stays for the shuffles; a token's lanes are all live or all not
+    float s[QQ], sel[QQ];
+#pragma unroll
+    for (int q = 0; q < QQ; ++q) s[q] = -INFINITY;
+    // z (or the logits) of this lane's experts
+    const float *src = part ? part : logits;
+    if (live) {
+        if (E % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < QQ; q += 4)
+                if (e0 + q < E) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + t * E + e0 + q);
+                    s[q] = v.x; s[q + 1] = v.y; s[q + 2] = v.z; s[q + 3] = v.w;
+                }
+            if (part)
+                for (int pi = 1; pi < nparts; ++pi) {
+#pragma unroll
+                    for (int q = 0; q < QQ; q += 4)
+                        if (e0 + q < E) {
+                            const float4 v = *reinterpret_cast<const float4 *>(part + pi * part_stride + t * E + e0 + q);
+                            s[q] += v.x; s[q + 1] += v.y; s[q + 2] += v.z; s[q + 3] += v.w;
+                        }
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < QQ; ++q)
+                if (e0 + q < E) {
+                    float z = src[t * E + e0 + q];
+                    if (part)
+                        for (int pi = 1; pi < nparts; ++pi) z += part[pi * part_stride + t * E + e0 + q];
+                    s[q] = z;
+                }
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        s[q] = -INFINITY;
+    for (int q = 0; q < QQ; ++q) {
+        const int e = e0 + q;
         sel[q] = -INFINITY;
-        if (e < E) {
+        if (live && e < E) {
             if (part) {
-                float z = part[t * E + e];
-                for (int pi = 1; pi < nparts; ++pi) z += part[pi * part_stride + t * E + e];
-                float v = __fmul_rn(z, scale);
+                float v = __fmul_rn(s[q], scale);
                 if (lbias) v = __fadd_rn(v, lbias[e]);
-                logits[t * E + e] = v;
                 s[q] = v;
-            } else {
-                s[q] = logits[t * E + e];
             }
             sel[q] = sbias ? __fadd_rn(s[q], sbias[e]) : s[q];
             mx = fmaxf(mx, s[q]);
         }
     }
-    mx = wave_max(mx);
+    if (part && live) {
+        if (E % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < QQ; q += 4)
+                if (e0 + q < E)
+                    *reinterpret_cast<float4 *>(logits + t * E + e0 + q) = make_float4(s[q], s[q + 1], s[q + 2], s[q + 3]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < QQ; ++q)
+                if (e0 + q < E) logits[t * E + e0 + q] = s[q];
+        }
+    }
+#pragma unroll
+    for (int off = LT / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     float den = 0.0f;
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-        if (lane + 64 * q < E) den += expf(s[q] - mx);
-    den = wave_sum(den);
+    for (int q = 0; q < QQ; ++q)
+        if (e0 + q < E) den += expf(s[q] - mx);
+#pragma unroll
+    for (int off = LT / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
     uint32_t taken = 0u;
     for (int j = 0; j < k; ++j) {
         float bv = 0.0f;
         int bi = 0x7fffffff;  // no candidate
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int e = lane + 64 * q;
+        for (int q = 0; q < QQ; ++q) {
+            const int e = e0 + q;
             if (e < E && !((taken >> q) & 1u) && (bi == 0x7fffffff || sel[q] > bv)) {
                 bv = sel[q];
                 bi = e;
             }
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
+        for (int off = LT / 2; off > 0; off >>= 1) {
             const float ov = __shfl_xor(bv, off, 64);
             const int oi = __shfl_xor(bi, off, 64);
             if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
@@ -87,11 +137,11 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
                 bi = oi;
             }
         }
-        if (lane == (bi & 63)) {
-            const int qb = bi >> 6;
+        if (live && r == bi / QQ) {
+            const int qb = bi % QQ;
             float sb = 0.0f;
 #pragma unroll
-            for (int q = 0; q < Q; ++q)
+            for (int q = 0; q < QQ; ++q)
                 if (q == qb) sb = s[q];
             taken |= 1u << qb;
             ids[t * k + j] = bi;
@@ -128,12 +178,19 @@ __global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__
         den += p[q];
     }
     den = wave_sum(den);
-    for (int j = 0; j < k; ++j) {
-        const int ej = ids[t * k + j];
-        const float gj = dw[t * ldw + j];
+    // the token's slots, 64 at a time: one coalesced load of ids and weight
+    // gradients per lane, then each slot broadcast from its lane
+    for (int jb = 0; jb < k; jb += 64) {
+        const int nj = min(64, k - jb);
+        const int e_lane = lane < nj ? ids[t * k + jb + lane] : -1;
+        const float g_lane = lane < nj ? dw[t * ldw + jb + lane] : 0.0f;
+        for (int j = 0; j < nj; ++j) {
+            const int ej = __shfl(e_lane, j, 64);
+            const float gj = __shfl(g_lane, j, 64);
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            if (lane + 64 * q == ej) g[q] = gj;
+            for (int q = 0; q < Q; ++q)
+                if (lane + 64 * q == ej) g[q] = gj;
+        }
     }
     float c = 0.0f;
 #pragma unroll
@@ -158,6 +215,12 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restri
     }
 }
 
+// Column tile of the two skinny products with E columns (the logits x . Wg
+// and Wg's gradient x^T . dz): one tile spans all E experts (up to 256), so x,
+// by far the largest operand, is read once.  With 64-column tiles, E = 160
+// read every row of x three times, in blocks that run on different XCDs.
+inline int col_tile(int E) { return E <= 64 ? 64 : E <= 128 ? 128 : 256; }
+
 inline int q_of(int E) {
     const int q = (E + 63) / 64;
     return q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : 16;
@@ -166,7 +229,8 @@ inline int q_of(int E) {
 // split count of the reduction over tokens for Wg's gradient: enough blocks to
 // fill the chip, at least 1024 tokens per split
 inline int rbwd_splits(int64_t T, int d, int E) {
-    const int64_t tiles = ((d + 127) / 128) * ((E + 63) / 64);
+    const int bn = col_tile(E);
+    const int64_t tiles = ((d + 127) / 128) * ((E + bn - 1) / bn);
     int64_t S = (512 + tiles - 1) / tiles;
     const int64_t maxS = (T + 255) / 256;
     if (S > maxS) S = maxS;
@@ -180,11 +244,14 @@ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255);
 }  // namespace
 
 // bf16 logits: the d reduction is split into kparts ranges so that the skinny
-// product (T x d times d x E) still gives the device a few hundred blocks; the
+// product (T x d times d x E) still gives each compute unit a block; the
 // partial sums land in the workspace and the top-k kernel adds them in order.
+// (Aiming at two blocks per compute unit doubles the partial sums written and
+// read again, and measured 4-10% slower at 128-256 experts.)
 int route_kparts(int64_t T, int d, int E) {
-    const int64_t tiles = ((T + 127) / 128) * ((E + 63) / 64);
-    int64_t kp = (512 + tiles - 1) / tiles;
+    const int bn = col_tile(E);
+    const int64_t tiles = ((T + 127) / 128) * ((E + bn - 1) / bn);
+    int64_t kp = (256 + tiles - 1) / tiles;
     const int64_t maxkp = d / 256;  // each part at least 256 of d
     if (kp > maxkp) kp = maxkp;
     if (kp < 1) kp = 1;
@@ -227,24 +294,36 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
         p.kparts = kparts;
         p.kpart_len = ((d / kparts + 31) / 32) * 32;
         p.c_gstride = T * E;
-        err = launch_gemm_dma<128, 64, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s);
+        switch (col_tile(E)) {
+            case 64: err = launch_gemm_dma<128, 64, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s); break;
+            case 128: err = launch_gemm_dma<128, 128, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s); break;
+            // E <= 192: four waves side by side over the 256 columns, so the
+            // wave whose 64 columns all lie past E skips its products
+            default:
+                err = E <= 192 ? launch_gemm_dma<128, 256, 32, 1, 4, 1, true, false, 3, EPI_STORE, float, 2>(p, s)
+                               : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, float, 2>(p, s);
+                break;
+        }
     } else {
         p.C0 = logits;
         err = launch_gemm_f32<1, true, false, EPI_ROUTER>(p, s);
     }
     if (err != hipSuccess) return err;
-    const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves)), block(256);
     const int64_t ps = T * E;
-#define XMOE_TOPK(Q)                                                                                          \
-    hipLaunchKernelGGL(topk_softmax_kernel<Q>, grid, block, 0, s, logits, part, kparts, ps, inv_tau, logit_bias, \
-                       select_bias, T, E, k, topk_ids, topk_w)
-    switch (q_of(E)) {
-        case 1: XMOE_TOPK(1); break;
-        case 2: XMOE_TOPK(2); break;
-        case 4: XMOE_TOPK(4); break;
-        case 8: XMOE_TOPK(8); break;
-        default: XMOE_TOPK(16); break;
-    }
+#define XMOE_TOPK(LT, QQ)                                                                                   \
+    hipLaunchKernelGGL((topk_softmax_kernel<LT, QQ>),                                                       \
+                       dim3(static_cast<unsigned>((T + kWaves * (64 / LT) - 1) / (kWaves * (64 / LT)))), dim3(256), \
+                       0, s, logits, part, kparts, ps, inv_tau, logit_bias, select_bias, T, E, k, topk_ids, topk_w)
+    // eight lanes per token up to 256 experts (at most 32 values a lane), then 16 and 32
+    if (E <= 32) XMOE_TOPK(8, 4);
+    else if (E <= 64) XMOE_TOPK(8, 8);
+    else if (E <= 96) XMOE_TOPK(8, 12);
+    else if (E <= 128) XMOE_TOPK(8, 16);
+    else if (E <= 160) XMOE_TOPK(8, 20);
+    else if (E <= 192) XMOE_TOPK(8, 24);
+    else if (E <= 256) XMOE_TOPK(8, 32);
+    else if (E <= 512) XMOE_TOPK(16, 32);
+    else XMOE_TOPK(32, 32);
 #undef XMOE_TOPK
     return hipGetLastError();
 }
@@ -327,8 +406,17 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
     b.C0 = part;
     b.ldc = E;
     b.c_gstride = static_cast<int64_t>(d) * E;
-    err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(b, s)
-                      : launch_gemm_dma<128, 64, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(b, s);
+    if (dt != kBF16)
+        err = launch_gemm_f32<1, false, false, EPI_STORE>(b, s);
+    else
+        switch (col_tile(E)) {
+            case 64: err = launch_gemm_dma<128, 64, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(b, s); break;
+            case 128: err = launch_gemm_dma<128, 128, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(b, s); break;
+            default:
+                err = E <= 192 ? launch_gemm_dma<128, 256, 32, 1, 4, 1, false, false, 3, EPI_STORE, float, 2>(b, s)
+                               : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(b, s);
+                break;
+        }
     if (err != hipSuccess) return err;
     const int64_t n = static_cast<int64_t>(d) * E;
     const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096));
