@@ -93,6 +93,32 @@ def test_router_bf16_small(xm, name):
     assert_close(host(w)[ok], r["topk_w"][ok], 1e-4, "topk_w")
 
 
+@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 384, 16), ("bf16", 130, 128, 1024, 8),
+                                          ("f32", 257, 64, 10, 3), ("f32", 100, 32, 300, 5),
+                                          ("f32", 64, 16, 1021, 4), ("f32", 33, 8, 1, 1)])
+def test_router_expert_counts(xm, dtype, T, d, E, k):
+    """Expert counts beyond the workloads': more than 256 experts (16 and 32
+    lanes per token in the top-k), fp32 counts that are not a multiple of 4
+    (element loads instead of 16-byte vectors), a single expert.  fp32 logits are
+    bit-exact, so its selections must match outright; bf16 through routing_check."""
+    x = workloads.random_rows(T, d, dtype, seed=E)
+    wg = workloads.random_rows(d, E, dtype, seed=E + 1, std=d ** -0.5)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    xm.xmoe_route(x.cuda(), wg.cuda(), k, ids, w, lg)
+    r = orc.route(orc_in(x), orc_in(wg), k, 0 if dtype == "f32" else 1)
+    if dtype == "f32":
+        np.testing.assert_array_equal(host(lg), r["scores"])
+        np.testing.assert_array_equal(host(ids), r["topk_ids"])
+        assert_close(host(w), r["topk_w"], 1e-5, "topk_w")
+        return
+    mism = routing_check(host(ids), host(lg), r, None, k, 1e-5)
+    ok = (host(ids) == r["topk_ids"]).all(axis=1) & ~mism
+    assert ok.sum() > 0.9 * T
+    assert_close(host(w)[ok], r["topk_w"][ok], 1e-4, "topk_w")
+
+
 # ------------------------------------------------------------------ PFT
 
 @pytest.mark.parametrize("T,E,k,skew", [(1, 8, 2, 0.0), (255, 8, 2, 0.0), (256, 64, 6, 0.0), (257, 64, 6, 0.0),
@@ -486,8 +512,12 @@ def test_expert_ffn_zero_rows(xm):
 # ------------------------------------------------------------------ router backward
 
 @pytest.mark.parametrize("dtype,T,d,E,k,inv_tau", [("f32", 256, 128, 8, 2, 1.0), ("bf16", 300, 256, 16, 6, 1.0),
-                                                   ("bf16", 2500, 512, 160, 8, 2.0), ("bf16", 777, 448, 64, 6, 1.0)])
+                                                   ("bf16", 2500, 512, 160, 8, 2.0), ("bf16", 777, 448, 64, 6, 1.0),
+                                                   ("bf16", 600, 256, 256, 8, 1.0), ("f32", 40, 32, 320, 70, 1.0),
+                                                   ("bf16", 64, 64, 512, 100, 0.5)])
 def test_route_bwd(xm, dtype, T, d, E, k, inv_tau):
+    """Includes 256 experts (the 2x2-wave 256-column tile of Wg's gradient), and
+    k above 64 (a token's slots read in two chunks)."""
     tdt = DT[dtype]
     g = torch.Generator().manual_seed(T + E)
     x = workloads.random_rows(T, d, dtype, seed=41)
