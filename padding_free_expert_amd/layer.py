@@ -231,8 +231,11 @@ class PaddingFreeMoE:
         main.wait_stream(gs)
         xmoe_dispatch_bwd(self.dxs, self.pft, self.T, self.dx, dx_add=dx_add, stream=main)
         mark("dispatch_bwd")
-        main.wait_stream(self.wside)  # every gradient is complete in the caller's stream order
-        main.wait_stream(self.gside)
+        # every gradient is complete in the caller's stream order (the gate's
+        # stream joined before the dispatch backward); only streams this call
+        # used are joined, so that the step can also be captured as a graph
+        if ws is not main:
+            main.wait_stream(ws)
         return self.dx
 
     def saved_bytes(self) -> int:
