@@ -310,20 +310,36 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
     }
     if (err != hipSuccess) return err;
     const int64_t ps = T * E;
+    // lanes per token: at most 32 experts a lane, and enough lanes that the
+    // launch gives each SIMD a few wavefronts (8 lanes from 32768 tokens on,
+    // 16 from 16384, else 32); a lane holds QQ, a multiple of 4, experts
+    const int lt_e = E <= 256 ? 8 : E <= 512 ? 16 : 32;
+    const int lt_t = T >= 32768 ? 8 : T >= 16384 ? 16 : 32;
+    const int lt = std::max(lt_e, lt_t);
+    const int qq = ((E + lt - 1) / lt + 3) / 4 * 4;
 #define XMOE_TOPK(LT, QQ)                                                                                   \
     hipLaunchKernelGGL((topk_softmax_kernel<LT, QQ>),                                                       \
                        dim3(static_cast<unsigned>((T + kWaves * (64 / LT) - 1) / (kWaves * (64 / LT)))), dim3(256), \
                        0, s, logits, part, kparts, ps, inv_tau, logit_bias, select_bias, T, E, k, topk_ids, topk_w)
-    // eight lanes per token up to 256 experts (at most 32 values a lane), then 16 and 32
-    if (E <= 32) XMOE_TOPK(8, 4);
-    else if (E <= 64) XMOE_TOPK(8, 8);
-    else if (E <= 96) XMOE_TOPK(8, 12);
-    else if (E <= 128) XMOE_TOPK(8, 16);
-    else if (E <= 160) XMOE_TOPK(8, 20);
-    else if (E <= 192) XMOE_TOPK(8, 24);
-    else if (E <= 256) XMOE_TOPK(8, 32);
-    else if (E <= 512) XMOE_TOPK(16, 32);
-    else XMOE_TOPK(32, 32);
+#define XMOE_TOPK_QQ(LT)                                                                                    \
+    switch (qq) {                                                                                           \
+        case 4: XMOE_TOPK(LT, 4); break;                                                                    \
+        case 8: XMOE_TOPK(LT, 8); break;                                                                    \
+        case 12: XMOE_TOPK(LT, 12); break;                                                                  \
+        case 16: XMOE_TOPK(LT, 16); break;                                                                  \
+        case 20: XMOE_TOPK(LT, 20); break;                                                                  \
+        case 24: XMOE_TOPK(LT, 24); break;                                                                  \
+        case 28: XMOE_TOPK(LT, 28); break;                                                                  \
+        default: XMOE_TOPK(LT, 32); break;                                                                  \
+    }
+    if (lt == 8) {
+        XMOE_TOPK_QQ(8)
+    } else if (lt == 16) {
+        XMOE_TOPK_QQ(16)
+    } else {
+        XMOE_TOPK_QQ(32)
+    }
+#undef XMOE_TOPK_QQ
 #undef XMOE_TOPK
     return hipGetLastError();
 }
