@@ -194,3 +194,38 @@ def test_identity_like_combine_k_equals_E(xm):
     fwd = orc.layer_forward(o, wl.k, 1)
     assert (layer.pft.tokens_per_expert.cpu().numpy() == wl.T).all()
     assert_close(host(layer.y), fwd["y"], RTOL["bf16"], "y")
+
+
+@pytest.mark.parametrize("merge", [False, True], ids=["shared-apart", "shared-merged"])
+def test_layer_step_replays_as_graph(xm, merge):
+    """The library allocates, clears and synchronises nothing, so one layer step
+    (forward and backward, all three streams) can be captured as a HIP graph.
+    Every replay, with eager steps run between replays, gives bitwise the
+    outputs and gradients of an eager step."""
+    wl = workloads.small("dsmoe16b")
+    inp = workloads.generate(wl, backward=True)
+    layer = run_layer(xm, wl, inp, merge=merge)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    ref = {"y": layer.y.clone(), **{k: v.clone() for k, v in layer.grads().items()}}
+
+    def outs():
+        return {"y": layer.y, **layer.grads()}
+
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cs):
+        layer.forward(g["x"])
+        layer.backward(g["dy"])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in outs().values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, t in outs().items():
+            assert torch.equal(t, ref[key]), key
+        layer.forward(g["x"])   # eager work between replays
+        layer.backward(g["dy"])
+        torch.cuda.synchronize()
