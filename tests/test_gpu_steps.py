@@ -95,11 +95,13 @@ def test_router_bf16_small(xm, name):
 
 @pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 384, 16), ("bf16", 130, 128, 1024, 8),
                                           ("f32", 257, 64, 10, 3), ("f32", 100, 32, 300, 5),
-                                          ("f32", 64, 16, 1021, 4), ("f32", 33, 8, 1, 1)])
+                                          ("f32", 64, 16, 1021, 4), ("f32", 33, 8, 1, 1),
+                                          ("bf16", 1, 2048, 160, 8), ("bf16", 7, 7168, 256, 8)])
 def test_router_expert_counts(xm, dtype, T, d, E, k):
     """Expert counts beyond the workloads': more than 256 experts (16 and 32
     lanes per token in the top-k), fp32 counts that are not a multiple of 4
-    (element loads instead of 16-byte vectors), a single expert.  fp32 logits are
+    (element loads instead of 16-byte vectors), a single expert; and a few
+    tokens, where the logits' d reduction is split into the most parts.  fp32 logits are
     bit-exact, so its selections must match outright; bf16 through routing_check."""
     x = workloads.random_rows(T, d, dtype, seed=E)
     wg = workloads.random_rows(d, E, dtype, seed=E + 1, std=d ** -0.5)
@@ -115,7 +117,7 @@ def test_router_expert_counts(xm, dtype, T, d, E, k):
         return
     mism = routing_check(host(ids), host(lg), r, None, k, 1e-5)
     ok = (host(ids) == r["topk_ids"]).all(axis=1) & ~mism
-    assert ok.sum() > 0.9 * T
+    assert ok.sum() >= 0.9 * T
     assert_close(host(w)[ok], r["topk_w"][ok], 1e-4, "topk_w")
 
 
