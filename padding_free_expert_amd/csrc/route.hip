@@ -27,8 +27,10 @@ namespace {
 constexpr int kWaves = 4;
 
 // LT lanes per token (8, 16 or 32), 64 / LT tokens per wavefront; lane r of a
-// token holds the QQ consecutive experts r*QQ .. r*QQ+QQ-1, read as 16-byte
-// vectors when E is a multiple of 4 (QQ always is).  When `part` is set, the
+// token holds QQ experts as 16-byte chunks r, r + LT, r + 2 LT, ... of the
+// token's row (expert of value q: 4 (r + LT (q / 4)) + q % 4, ascending in q),
+// so that every load and store instruction covers one contiguous run of the
+// row; the vectors are used when E is a multiple of 4 (QQ always is).  When `part` is set, the
 // logits are first formed from nparts fp32 partial sums of z (a split of the
 // d reduction, summed in part order), then scaled and biased with one IEEE
 // operation each and written to `logits`.  The softmax and the top-k (k
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
     constexpr int TPW = 64 / LT;
     const int lane = threadIdx.x & 63;
     const int r = lane % LT;
-    const int e0 = r * QQ;
+    auto ex = [&](int q) { return 4 * (r + LT * (q >> 2)) + (q & 3); };  // expert of value q
     const int64_t t = (static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * TPW + lane / LT;
     const bool live = t < T;  // every lane stays for the shuffles; a token's lanes are all live or all not
     float s[QQ], sel[QQ];
@@ -57,26 +59,26 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
         if (E % 4 == 0) {
 #pragma unroll
             for (int q = 0; q < QQ; q += 4)
-                if (e0 + q < E) {
-                    const float4 v = *reinterpret_cast<const float4 *>(src + t * E + e0 + q);
+                if (ex(q) < E) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + t * E + ex(q));
                     s[q] = v.x; s[q + 1] = v.y; s[q + 2] = v.z; s[q + 3] = v.w;
                 }
             if (part)
                 for (int pi = 1; pi < nparts; ++pi) {
 #pragma unroll
                     for (int q = 0; q < QQ; q += 4)
-                        if (e0 + q < E) {
-                            const float4 v = *reinterpret_cast<const float4 *>(part + pi * part_stride + t * E + e0 + q);
+                        if (ex(q) < E) {
+                            const float4 v = *reinterpret_cast<const float4 *>(part + pi * part_stride + t * E + ex(q));
                             s[q] += v.x; s[q + 1] += v.y; s[q + 2] += v.z; s[q + 3] += v.w;
                         }
                 }
         } else {
 #pragma unroll
             for (int q = 0; q < QQ; ++q)
-                if (e0 + q < E) {
-                    float z = src[t * E + e0 + q];
+                if (ex(q) < E) {
+                    float z = src[t * E + ex(q)];
                     if (part)
-                        for (int pi = 1; pi < nparts; ++pi) z += part[pi * part_stride + t * E + e0 + q];
+                        for (int pi = 1; pi < nparts; ++pi) z += part[pi * part_stride + t * E + ex(q)];
                     s[q] = z;
                 }
         }
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
     float mx = -INFINITY;
 #pragma unroll
     for (int q = 0; q < QQ; ++q) {
-        const int e = e0 + q;
+        const int e = ex(q);
         sel[q] = -INFINITY;
         if (live && e < E) {
             if (part) {
@@ -100,12 +102,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
         if (E % 4 == 0) {
 #pragma unroll
             for (int q = 0; q < QQ; q += 4)
-                if (e0 + q < E)
-                    *reinterpret_cast<float4 *>(logits + t * E + e0 + q) = make_float4(s[q], s[q + 1], s[q + 2], s[q + 3]);
+                if (ex(q) < E)
+                    *reinterpret_cast<float4 *>(logits + t * E + ex(q)) = make_float4(s[q], s[q + 1], s[q + 2], s[q + 3]);
         } else {
 #pragma unroll
             for (int q = 0; q < QQ; ++q)
-                if (e0 + q < E) logits[t * E + e0 + q] = s[q];
+                if (ex(q) < E) logits[t * E + ex(q)] = s[q];
         }
     }
 #pragma unroll
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
     float den = 0.0f;
 #pragma unroll
     for (int q = 0; q < QQ; ++q)
-        if (e0 + q < E) den += expf(s[q] - mx);
+        if (ex(q) < E) den += expf(s[q] - mx);
 #pragma unroll
     for (int off = LT / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
     uint32_t taken = 0u;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
         int bi = 0x7fffffff;  // no candidate
 #pragma unroll
         for (int q = 0; q < QQ; ++q) {
-            const int e = e0 + q;
+            const int e = ex(q);
             if (e < E && !((taken >> q) & 1u) && (bi == 0x7fffffff || sel[q] > bv)) {
                 bv = sel[q];
                 bi = e;
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
                 bi = oi;
             }
         }
-        if (live && r == bi / QQ) {
-            const int qb = bi % QQ;
+        if (live && r == (bi >> 2) % LT) {
+            const int qb = ((bi >> 2) / LT) * 4 + (bi & 3);
             float sb = 0.0f;
 #pragma unroll
             for (int q = 0; q < QQ; ++q)
