@@ -152,60 +152,81 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(float *__restrict__ l
     }
 }
 
-template <int Q, typename OutT>
+// dz = p * (g - c) * inv_tau per token (p = softmax of the logits, g the
+// slots' weight gradients scattered to their experts, c = sum of p * g), with
+// the top-k kernel's layout: LT lanes per token, lane r holding the 16-byte
+// chunks r, r + LT, ... of the token's row.  The token's slots arrive LT at a
+// time, one per lane, and are broadcast within the token's lanes.
+template <int LT, int QQ, typename OutT>
 __global__ __launch_bounds__(256) void route_dz_kernel(const float *__restrict__ logits,
                                                        const int32_t *__restrict__ ids,
                                                        const float *__restrict__ dw, int ldw, int64_t T, int E,
                                                        int k, float inv_tau, OutT *__restrict__ dz) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (t >= T) return;
+    static_assert(LT == 8 || LT == 16 || LT == 32, "lanes per token");
+    static_assert(QQ % 4 == 0, "whole 16-byte chunks");
+    constexpr int TPW = 64 / LT;
     const int lane = threadIdx.x & 63;
-    float p[Q], g[Q];
-    float mx = -INFINITY;
+    const int r = lane % LT, g0 = lane - r;  // lane r of the token's group starting at g0
+    auto ex = [&](int q) { return 4 * (r + LT * (q >> 2)) + (q & 3); };
+    const int64_t t = (static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6)) * TPW + lane / LT;
+    const bool live = t < T;  // a token's lanes are all live or all not
+    float p[QQ], g[QQ];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
+    for (int q = 0; q < QQ; ++q) {
         p[q] = -INFINITY;
         g[q] = 0.0f;
-        if (e < E) {
-            p[q] = logits[t * E + e];
-            mx = fmaxf(mx, p[q]);
+    }
+    if (live) {
+        if (E % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < QQ; q += 4)
+                if (ex(q) < E) {
+                    const float4 v = *reinterpret_cast<const float4 *>(logits + t * E + ex(q));
+                    p[q] = v.x; p[q + 1] = v.y; p[q + 2] = v.z; p[q + 3] = v.w;
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < QQ; ++q)
+                if (ex(q) < E) p[q] = logits[t * E + ex(q)];
         }
     }
-    mx = wave_max(mx);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < QQ; ++q) mx = fmaxf(mx, p[q]);
+#pragma unroll
+    for (int off = LT / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     float den = 0.0f;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        p[q] = (lane + 64 * q < E) ? expf(p[q] - mx) : 0.0f;
+    for (int q = 0; q < QQ; ++q) {
+        p[q] = ex(q) < E && live ? expf(p[q] - mx) : 0.0f;
         den += p[q];
     }
-    den = wave_sum(den);
-    // the token's slots, 64 at a time: one coalesced load of ids and weight
-    // gradients per lane, then each slot broadcast from its lane
-    for (int jb = 0; jb < k; jb += 64) {
-        const int nj = min(64, k - jb);
-        const int e_lane = lane < nj ? ids[t * k + jb + lane] : -1;
-        const float g_lane = lane < nj ? dw[t * ldw + jb + lane] : 0.0f;
-        for (int j = 0; j < nj; ++j) {
-            const int ej = __shfl(e_lane, j, 64);
-            const float gj = __shfl(g_lane, j, 64);
 #pragma unroll
-            for (int q = 0; q < Q; ++q)
-                if (lane + 64 * q == ej) g[q] = gj;
+    for (int off = LT / 2; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+    for (int jb = 0; jb < k; jb += LT) {
+        const int nj = min(LT, k - jb);
+        const int e_lane = live && r < nj ? ids[t * k + jb + r] : -1;
+        const float g_lane = live && r < nj ? dw[t * ldw + jb + r] : 0.0f;
+        for (int j = 0; j < nj; ++j) {
+            const int ej = __shfl(e_lane, g0 + j, 64);
+            const float gj = __shfl(g_lane, g0 + j, 64);
+#pragma unroll
+            for (int q = 0; q < QQ; ++q)
+                if (ex(q) == ej) g[q] = gj;
         }
     }
     float c = 0.0f;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
+    for (int q = 0; q < QQ; ++q) {
         p[q] /= den;
         c += p[q] * g[q];
     }
-    c = wave_sum(c);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int e = lane + 64 * q;
-        if (e < E) Elem<OutT>::store(dz, t * E + e, p[q] * (g[q] - c) * inv_tau);
-    }
+    for (int off = LT / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (!live) return;
+#pragma unroll
+    for (int q = 0; q < QQ; ++q)
+        if (ex(q) < E) Elem<OutT>::store(dz, t * E + ex(q), p[q] * (g[q] - c) * inv_tau);
 }
 
 __global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restrict__ part, int S, int64_t n,
@@ -223,9 +244,13 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restri
 // read every row of x three times, in blocks that run on different XCDs.
 inline int col_tile(int E) { return E <= 64 ? 64 : E <= 128 ? 128 : 256; }
 
-inline int q_of(int E) {
-    const int q = (E + 63) / 64;
-    return q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : 16;
+// Lanes per token of the top-k and dz kernels: at most 32 experts a lane, and
+// enough lanes that the launch gives each SIMD a few wavefronts (8 lanes from
+// 32768 tokens on, 16 from 16384, else 32).
+inline int lanes_per_token(int64_t T, int E) {
+    const int lt_e = E <= 256 ? 8 : E <= 512 ? 16 : 32;
+    const int lt_t = T >= 32768 ? 8 : T >= 16384 ? 16 : 32;
+    return std::max(lt_e, lt_t);
 }
 
 // split count of the reduction over tokens for Wg's gradient: enough blocks to
@@ -312,12 +337,8 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
     }
     if (err != hipSuccess) return err;
     const int64_t ps = T * E;
-    // lanes per token: at most 32 experts a lane, and enough lanes that the
-    // launch gives each SIMD a few wavefronts (8 lanes from 32768 tokens on,
-    // 16 from 16384, else 32); a lane holds QQ, a multiple of 4, experts
-    const int lt_e = E <= 256 ? 8 : E <= 512 ? 16 : 32;
-    const int lt_t = T >= 32768 ? 8 : T >= 16384 ? 16 : 32;
-    const int lt = std::max(lt_e, lt_t);
+    // a lane holds QQ, a multiple of 4, experts
+    const int lt = lanes_per_token(T, E);
     const int qq = ((E + lt - 1) / lt + 3) / 4 * 4;
 #define XMOE_TOPK(LT, QQ)                                                                                   \
     hipLaunchKernelGGL((topk_softmax_kernel<LT, QQ>),                                                       \
@@ -354,15 +375,34 @@ size_t route_bwd_workspace(int64_t T, int d, int E, int dt) {
 }
 
 template <typename OutT>
-static void launch_dz(int E, dim3 grid, hipStream_t s, const float *logits, const int32_t *ids, const float *dw,
-                      int ldw, int64_t T, int k, float inv_tau, OutT *dz) {
-    switch (q_of(E)) {
-        case 1: hipLaunchKernelGGL((route_dz_kernel<1, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
-        case 2: hipLaunchKernelGGL((route_dz_kernel<2, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
-        case 4: hipLaunchKernelGGL((route_dz_kernel<4, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
-        case 8: hipLaunchKernelGGL((route_dz_kernel<8, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
-        default: hipLaunchKernelGGL((route_dz_kernel<16, OutT>), grid, dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz); break;
+static void launch_dz(int E, hipStream_t s, const float *logits, const int32_t *ids, const float *dw, int ldw,
+                      int64_t T, int k, float inv_tau, OutT *dz) {
+    const int lt = lanes_per_token(T, E);
+    const int qq = ((E + lt - 1) / lt + 3) / 4 * 4;
+#define XMOE_DZ(LT, QQ)                                                                                       \
+    hipLaunchKernelGGL((route_dz_kernel<LT, QQ, OutT>),                                                       \
+                       dim3(static_cast<unsigned>((T + kWaves * (64 / LT) - 1) / (kWaves * (64 / LT)))),      \
+                       dim3(256), 0, s, logits, ids, dw, ldw, T, E, k, inv_tau, dz)
+#define XMOE_DZ_QQ(LT)                                                                                        \
+    switch (qq) {                                                                                             \
+        case 4: XMOE_DZ(LT, 4); break;                                                                        \
+        case 8: XMOE_DZ(LT, 8); break;                                                                        \
+        case 12: XMOE_DZ(LT, 12); break;                                                                      \
+        case 16: XMOE_DZ(LT, 16); break;                                                                      \
+        case 20: XMOE_DZ(LT, 20); break;                                                                      \
+        case 24: XMOE_DZ(LT, 24); break;                                                                      \
+        case 28: XMOE_DZ(LT, 28); break;                                                                      \
+        default: XMOE_DZ(LT, 32); break;                                                                      \
     }
+    if (lt == 8) {
+        XMOE_DZ_QQ(8)
+    } else if (lt == 16) {
+        XMOE_DZ_QQ(16)
+    } else {
+        XMOE_DZ_QQ(32)
+    }
+#undef XMOE_DZ_QQ
+#undef XMOE_DZ
 }
 
 hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *logits, const int32_t *topk_ids,
@@ -374,11 +414,10 @@ hipError_t launch_route_bwd(int dt, const void *x, const void *wg, const float *
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + dz_bytes);
     hipError_t err;
     if (T > 0) {
-        const dim3 grid(static_cast<unsigned>((T + kWaves - 1) / kWaves));
         if (dt == kBF16)
-            launch_dz<bf16_t>(E, grid, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<bf16_t *>(dz));
+            launch_dz<bf16_t>(E, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<bf16_t *>(dz));
         else
-            launch_dz<float>(E, grid, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<float *>(dz));
+            launch_dz<float>(E, s, logits, topk_ids, dtopk_w, ldw, T, k, inv_tau, static_cast<float *>(dz));
         if ((err = hipGetLastError()) != hipSuccess) return err;
 
         // dx[t] += dz[t] . Wg^T (or dx[t] = ... without accumulate) : A = dz [T,E]
