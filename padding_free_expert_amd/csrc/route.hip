@@ -8,12 +8,12 @@
 // the lower expert index, and the chosen probabilities as (unrenormalised)
 // combine weights.
 //
-// Forward: one product x . Wg whose epilogue applies the scale and bias and
-// stores the fp32 scores, then one wavefront per token for softmax + top-k
-// (k rounds of a wavefront-wide arg-max under the order (sel desc, index asc)).
-// Backward: one wavefront per token forms dz = p * (g - c) * inv_tau; two
-// products then give dx += dz . Wg^T and the split-T partials of Wg's gradient,
-// which a last kernel sums in a fixed order.
+// Forward: one product x . Wg (bf16: split over d, fp32 partial sums) whose
+// column tile spans all experts, then softmax + top-k with 8-32 lanes per
+// token (k rounds of an arg-max over the token's lanes under the order (sel
+// desc, index asc)).  Backward: the same lane layout forms dz = p * (g - c) *
+// inv_tau; two products then give dx += dz . Wg^T and the split-T partials of
+// Wg's gradient, which a last kernel sums in a fixed order.
 #include <algorithm>
 
 #include "common.hpp"
