@@ -39,16 +39,23 @@ def _sub(t: torch.Tensor, idx) -> np.ndarray:
     return orc_in(t[torch.as_tensor(idx, device=t.device, dtype=torch.long)])
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "dsmoe16b", "dsv3", "zipf_skew", "long_batch"])
-def test_full_size_layer(xm, name):
+CASES = [(n, False, False) for n in ["tiny_f32", "dsmoe16b", "dsv3", "zipf_skew", "long_batch"]] + \
+        [("dsmoe16b", True, True)]
+
+
+@pytest.mark.parametrize("name,lean,merge", CASES,
+                         ids=[n + ("-lean-shared-merged" if lean else "") for n, lean, _ in CASES])
+def test_full_size_layer(xm, name, lean, merge):
+    """lean: H1/H3 recomputed in the backward instead of kept; merge: the shared
+    experts carried as always-routed experts in the routed buffer."""
     from padding_free_expert_amd.layer import PaddingFreeMoE
     wl = workloads.get(name)
-    print(f"\n[{name}] T={wl.T} d={wl.d} E={wl.E} h={wl.h} k={wl.k}", flush=True)
+    print(f"\n[{name}] T={wl.T} d={wl.d} E={wl.E} h={wl.h} k={wl.k} lean={lean} merge={merge}", flush=True)
     inp = workloads.generate(wl, device="cuda", backward=True)
     weights = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias")
                if k in inp}
     bwd_on = True
-    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=bwd_on)
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=bwd_on, lean=lean, merge_shared=merge)
     layer.forward(inp["x"])
     layer.backward(inp["dy"])
     torch.cuda.synchronize()
