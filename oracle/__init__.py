@@ -277,18 +277,27 @@ def _shared_slices(s1, s3, s2, n_shared: int):
 
 def layer_forward(inp: Dict[str, np.ndarray], k: int, mode: int, inv_tau: float = 1.0,
                   n_shared: int = 0, tokens: Optional[np.ndarray] = None,
-                  expert_subset: Optional[np.ndarray] = None):
+                  expert_subset: Optional[np.ndarray] = None, select: Optional[Dict[int, np.ndarray]] = None):
     """Forward of the whole layer for every token (or only `tokens`).
 
     Y[t] = sum_{j} p[t, S_t(j)] * FFN_{S_t(j)}(X[t]) + sum_s FFN^shared_s(X[t]).
     With expert_subset (sorted expert ids), inp's w1/w3/w2 hold only those
     experts, in that order; every routed expert must be in the subset.
+    select {t: ids[k]}: token t's selection is taken as given instead of the
+    oracle's own (for a near-tie, where more than one selection is correct);
+    its weights are still the oracle's probabilities of those experts.
     Returns a dict with the routing, the per-slot expert outputs and y."""
     x = inp["x"]
     if tokens is not None:
         x = np.ascontiguousarray(x[tokens])
     T = x.shape[0]
     r = route(x, inp["wg"], k, mode, inv_tau, inp.get("logit_bias"), inp.get("select_bias"))
+    for t, ids in (select or {}).items():
+        ids = np.asarray(ids, np.int32)
+        if ids.shape != (k,) or len(set(ids.tolist())) != k or ids.min() < 0 or ids.max() >= r["probs"].shape[1]:
+            raise OracleError(f"select: token {t} needs {k} distinct experts")
+        r["topk_ids"][t] = ids
+        r["topk_w"][t] = r["probs"][t, ids]
     row_token = np.repeat(np.arange(T, dtype=np.int32), k)
     row_expert = r["topk_ids"].reshape(-1)
     if expert_subset is not None:

@@ -20,6 +20,19 @@ import torch
 
 RTOL = {"f32": 1e-4, "bf16": 2e-2}
 
+# Bound on the tokens whose GPU selection differs from the oracle's inside a
+# near-tie (both correct; see routing_check), per workload.  Measured: 0-1.
+NEAR_TIE_MAX = 8
+
+# Lines printed at the end of the pytest run (tests/conftest.py), so that a
+# quiet run still shows the near-tie counts and how much of each tolerance the
+# outputs use.
+REPORT: list = []
+
+
+def report(line: str) -> None:
+    REPORT.append(line)
+
 
 def need_gpu():
     if not torch.cuda.is_available():
@@ -57,7 +70,7 @@ def assert_close(got, ref, rtol: float, name: str = "", floor=None):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite output"
     if ref.size == 0:
-        return
+        return {"elem": 0.0, "norm": 0.0}
     rms = float(np.sqrt(np.mean(ref * ref)))
     err = np.abs(got - ref)
     lim = rtol * (np.abs(ref) + (rms if floor is None else np.asarray(floor, np.float64)))
@@ -68,12 +81,18 @@ def assert_close(got, ref, rtol: float, name: str = "", floor=None):
         raise AssertionError(f"{name}: {int(bad.sum())}/{err.size} elements beyond tolerance; worst at {i}: "
                              f"got {got[i]!r} ref {ref[i]!r} (floor {fl:.3e}, rms {rms:.3e}, rtol {rtol})")
     nrm = float(np.linalg.norm(ref))
+    rel = 0.0
     if nrm > 0:
         rel = float(np.linalg.norm(got - ref)) / nrm
         assert rel <= rtol, f"{name}: normwise relative error {rel:.3e} > {rtol}"
+    # the largest err / limit over the elements (1.0 = at the tolerance) and
+    # the normwise error as a fraction of rtol
+    used = float(np.max(np.where(lim > 0, err / np.where(lim > 0, lim, 1.0), 0.0)))
+    return {"elem": used, "norm": rel / rtol}
 
 
-def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias, k: int, score_tol: float):
+def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias, k: int, score_tol: float,
+                  stats: dict = None):
     """Compare the GPU's top-k with the oracle's.
 
     Both sides decide in fp32 on their own logits; the GPU's logits may differ
@@ -100,6 +119,8 @@ def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias,
     ambiguous = (gaps.min(axis=1) <= delta) if gaps.shape[1] else np.zeros(T, bool)
     oid = orc["topk_ids"]
     clear = ~ambiguous
+    if stats is not None:
+        stats.update(delta=delta, ambiguous=int(ambiguous.sum()))
     np.testing.assert_array_equal(gpu_ids[clear], oid[clear])
     mismatch = np.zeros(T, bool)
     for t in np.nonzero(ambiguous)[0]:
@@ -113,7 +134,31 @@ def routing_check(gpu_ids: np.ndarray, gpu_logits: np.ndarray, orc, select_bias,
         assert set(must.tolist()) <= set(g.tolist()), (t, must, g)
         assert (np.diff(gs) <= delta).all(), (t, gs)
         mismatch[t] = set(g.tolist()) != set(oid[t].tolist())
+    if stats is not None:
+        stats["mismatch"] = int(mismatch.sum())
     return mismatch
+
+
+def near_tie_bound(name: str, stats: dict, T: int) -> None:
+    """Report the near-tie counts and hold the differently routed ones to
+    NEAR_TIE_MAX."""
+    report(f"{name}: near-tied tokens {stats['ambiguous']}, routed differently {stats['mismatch']} of {T} "
+           f"(bound {NEAR_TIE_MAX}; delta {stats['delta']:.2e})")
+    assert stats["mismatch"] <= NEAR_TIE_MAX, \
+        f"{name}: {stats['mismatch']} tokens routed differently inside near-ties (bound {NEAR_TIE_MAX})"
+
+
+def pft_contract(pft: dict, ids: np.ndarray, w: np.ndarray, E: int, orc_mod) -> None:
+    """The buffer given its routing: the oracle's construction from the same
+    (ids, w) must equal the device's buffer in all six fields, bit for bit,
+    whatever the near-ties (the buffer is a function of the routing alone),
+    and the buffer must have every property of a valid one."""
+    ref = orc_mod.build_pft(ids, np.asarray(w, np.float32), E)
+    for key in ("token_ids", "expert_ids", "tokens_per_expert", "expert_offsets", "slot_to_row"):
+        np.testing.assert_array_equal(pft[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(pft["combine_weights"].view(np.uint32), ref["combine_weights"].view(np.uint32),
+                                  err_msg="combine_weights")
+    pft_invariants(ids, w, E, pft)
 
 
 def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2):
@@ -140,11 +185,18 @@ def assert_wgrad_close(got, ref, rows_of, floors_of, rtol: float, name: str):
     without rows.  rows_of(e) -> number of rows; floors_of(e) -> floor array."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    worst = {"elem": 0.0, "norm": 0.0}
     for e in range(ref.shape[0]):
         if rows_of(e) == 0:
             assert (got[e] == 0).all(), f"{name}[{e}]: expert without rows must get a zero gradient"
             continue
-        assert_close(got[e], ref[e], rtol, f"{name}[{e}]", floor=floors_of(e))
+        u = assert_close(got[e], ref[e], rtol, f"{name}[{e}]", floor=floors_of(e))
+        worst = {key: max(worst[key], u[key]) for key in worst}
+    return worst
+
+
+def used_str(used: dict) -> str:
+    return f"{used['elem']:.2f}/{used['norm']:.2f}"
 
 
 def by_expert(ids: np.ndarray, vals: np.ndarray) -> np.ndarray:
@@ -175,7 +227,16 @@ def pft_invariants(ids: np.ndarray, w: np.ndarray, E: int, pft: dict):
     T, k = ids.shape
     R = T * k
     tpe, off = pft["tokens_per_expert"], pft["expert_offsets"]
+    eid = pft["expert_ids"]
+    assert tpe.shape == (E,) and off.shape == (E + 1,) and eid.shape == (R,)
     assert tpe.sum() == R and off[0] == 0 and off[-1] == R and (np.diff(off) == tpe).all()
+    # the counts are those of the rows' experts, and each expert's segment
+    # [off[e], off[e+1]) holds exactly its rows
+    assert eid.min(initial=0) >= 0 and eid.max(initial=0) < E
+    np.testing.assert_array_equal(tpe, np.bincount(eid, minlength=E), err_msg="tokens_per_expert")
+    np.testing.assert_array_equal(eid, np.repeat(np.arange(E, dtype=eid.dtype), tpe), err_msg="expert segments")
+    np.testing.assert_array_equal(tpe, np.bincount(np.asarray(ids).reshape(-1), minlength=E),
+                                  err_msg="tokens_per_expert against the routing")
     assert (np.bincount(pft["token_ids"], minlength=T) == k).all()
     assert np.unique(pft["token_ids"].astype(np.int64) * E + pft["expert_ids"]).size == R
     assert (np.diff(pft["expert_ids"]) >= 0).all()

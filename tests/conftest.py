@@ -18,3 +18,16 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Near-tie counts and the worst used fraction of each tolerance
+    (elementwise err/limit, then normwise err/rtol) of the GPU parity tests."""
+    try:
+        from _helpers import REPORT
+    except ImportError:
+        return
+    if REPORT:
+        terminalreporter.write_line("parity report (used tolerance: elementwise / normwise):")
+        for line in REPORT:
+            terminalreporter.write_line("  " + line)

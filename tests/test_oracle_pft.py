@@ -101,3 +101,50 @@ def test_zipf_workload_load_shape(orc):
     assert tpe.sum() == wl.T * wl.k
     assert (tpe == 0).sum() > 0
     assert tpe.max() > 10 * tpe.mean()
+
+
+def _corruptions(out):
+    """Buffers that break one property each, built from a valid one."""
+    bad = []
+
+    def mod(key, f):
+        o = {k: v.copy() for k, v in out.items()}
+        f(o[key])
+        bad.append((key, o))
+
+    # counts and offsets that no longer match the rows' experts (totals kept)
+    def shift_count(a):
+        a[0] += 1
+        a[1] -= 1
+    mod("tokens_per_expert", shift_count)
+    o = {k: v.copy() for k, v in out.items()}
+    shift_count(o["tokens_per_expert"])
+    o["expert_offsets"][1:] = np.cumsum(o["tokens_per_expert"])
+    bad.append(("tokens_per_expert+offsets", o))
+    mod("expert_ids", lambda a: a.__setitem__(0, a[-1]))      # a row in the wrong expert
+    mod("token_ids", lambda a: a.__setitem__(slice(0, 2), a[1::-1].copy()))  # order inside a segment
+    mod("slot_to_row", lambda a: a.__setitem__(slice(0, 2), a[1::-1].copy()))
+    mod("combine_weights", lambda a: a.__setitem__(0, np.nextafter(a[0], np.float32(2))))
+    return bad
+
+
+def test_gpu_side_invariant_check_catches_corruptions(orc):
+    """The validity check the GPU tests apply to the device's buffer (tests/
+    _helpers.pft_invariants) accepts the oracle's buffer and rejects each
+    planted corruption, including counts that disagree with the expert
+    segments while their sum and scan stay consistent."""
+    from _helpers import pft_invariants
+    ids_t, w_t = workloads.random_topk(40, 6, 2, seed=3)
+    ids, w = ids_t.numpy(), w_t.numpy()
+    out = orc.build_pft(ids, w, 6)
+    pft_invariants(ids, w, 6, out)
+    for what, o in _corruptions(out):
+        with pytest.raises(AssertionError):
+            pft_invariants(ids, w, 6, o)
+            print("not caught:", what)
+    # the counterexample of four rows: expert_ids [0,0,1,1] with counts [3,1]
+    four = {"token_ids": np.arange(4, dtype=np.int32), "expert_ids": np.array([0, 0, 1, 1], np.int32),
+            "tokens_per_expert": np.array([3, 1], np.int32), "expert_offsets": np.array([0, 3, 4], np.int32),
+            "combine_weights": np.ones(4, np.float32), "slot_to_row": np.arange(4, dtype=np.int32)}
+    with pytest.raises(AssertionError):
+        pft_invariants(np.array([[0], [0], [1], [1]], np.int32), np.ones((4, 1), np.float32), 2, four)
