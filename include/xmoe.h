@@ -192,13 +192,15 @@ xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, x
                                int32_t h, void *act, void *h13, void *stream);
 
 /*
- * Down-projection: ye[r] = act[r] . w2[e] for the rows of expert e
- * (w2 [E,h,d], act [rows,h], ye [rows,d]).  Same offsets and limits as
- * xmoe_expert_ffn_up.
+ * Down-projection (X-MoE article, section 2.1.2: each expert's own rows):
+ * ye[r] = act[r] . w2[e] for the rows of expert e (w2 [E,h,d], act [rows,h],
+ * ye [rows,d]).  accumulate != 0: ye[r] += act[r] . w2[e] (ye read, the sum
+ * rounded once to the dtype); 0: ye is overwritten.  Same offsets and limits
+ * as xmoe_expert_ffn_up.
  */
 xmoe_status xmoe_expert_ffn_down(const void *act, const void *w2, xmoe_dtype dtype,
                                  const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d,
-                                 int32_t h, void *ye, void *stream);
+                                 int32_t h, void *ye, int32_t accumulate, void *stream);
 
 /*
  * Up-projection with the dispatch gather fused into the operand loads (X-MoE
@@ -218,26 +220,33 @@ xmoe_status xmoe_expert_ffn_up_gather(const void *x, const int32_t *token_ids, c
 
 /*
  * Whole expert FFN with the gather fused: xmoe_expert_ffn_up_gather followed
- * by xmoe_expert_ffn_down.  Same arguments and limits as those two calls.
+ * by xmoe_expert_ffn_down (accumulate as there).  Same arguments and limits as
+ * those two calls.
  */
 xmoe_status xmoe_expert_ffn_gather(const void *x, const int32_t *token_ids, const void *w1,
                                    const void *w3, const void *w2, xmoe_dtype dtype,
                                    const int32_t *expert_offsets, int32_t E, int64_t T,
                                    int64_t rows, int32_t d, int32_t h, void *act, void *h13,
-                                   void *ye, void *stream);
+                                   void *ye, int32_t accumulate, void *stream);
 
 /*
- * Whole expert FFN: xmoe_expert_ffn_up followed by xmoe_expert_ffn_down.
- * act [rows,h] is required (it is the down-projection's input and the
- * backward's); h13 may be NULL for a forward-only pass.
+ * Whole expert FFN ("5.4 MoE模型在分布式训练中的应用", section 训练流程: each
+ * expert processes the tokens dispatched to it; X-MoE article, section 2.1.2:
+ * over each expert's own rows, no padding): xmoe_expert_ffn_up followed by
+ * xmoe_expert_ffn_down.  act [rows,h] is required (it is the down-projection's
+ * input and the backward's); h13 may be NULL for a forward-only pass.
+ * accumulate != 0: ye += the expert outputs (one rounding of the sum), so
+ * several FFNs can add into one output; 0: ye is overwritten.
  * Shared (always-on) experts run through the same call with E = 1,
- * offsets = {0, T}, xs = x; several shared experts of width h_s are one call
- * of width n*h_s with their weights side by side along the hidden axis.
+ * offsets = {0, T}, xs = x: either one call per shared expert, the second with
+ * accumulate = 1, or -- faster -- one call of width n*h_s with the n experts'
+ * weights side by side along the hidden axis (the same sum: a SwiGLU FFN of
+ * width n*h_s is the sum of the n FFNs of its column blocks).
  */
 xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, const void *w2,
                             xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                             int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *ye,
-                            void *stream);
+                            int32_t accumulate, void *stream);
 
 /*
  * Combine ("5.4 MoE模型在分布式训练中的应用", section 专家并行: results return to
@@ -253,7 +262,10 @@ xmoe_status xmoe_combine(const void *ye, const xmoe_pft *pft, int64_t T, int32_t
 /* ----------------------------------------------------------------- backward */
 
 /*
- * Backward of the combine for the upstream gradient dy [T,d]:
+ * Backward of the combine ("5.4 MoE模型在分布式训练中的应用", section 训练流程:
+ * the backward runs the forward's steps in reverse; the combine there is the
+ * weighted sum of section 专家并行 with the X-MoE article's combine_weights,
+ * section 2.1.1) for the upstream gradient dy [T,d]:
  *   dye[r]        = combine_weights[r] * dy[token_ids[r]]          (dye [R,d])
  *   dtopk_w[t, j] = < dy[t], ye[slot_to_row[t*k+j]] >              (fp32 [T,k])
  * Token by token: dy[t] is read once.
@@ -263,42 +275,53 @@ xmoe_status xmoe_combine_bwd(const void *dy, const void *ye, const xmoe_pft *pft
                              void *stream);
 
 /*
- * Backward of the SwiGLU experts, per expert, given dye [rows,d]:
+ * Backward of the SwiGLU experts ("5.4 MoE模型在分布式训练中的应用", section
+ * 训练流程: the reverse path through the experts; X-MoE article, section 2.1.2:
+ * each expert over its own rows), per expert, given dye [rows,d]:
  *   dA  = dye . w2[e]^T
  *   dH1 = dA * H3 * sig(H1) * (1 + H1 * (1 - sig(H1))),  dH3 = dA * silu(H1)
  *         -> dh13 = [dH1 | dH3]                                   (dh13 [rows,2h])
  *   dxs = dH1 . w1[e]^T + dH3 . w3[e]^T                           (dxs [rows,d])
  *   dw1[e] = xs_e^T . dH1,  dw3[e] = xs_e^T . dH3                (dw1, dw3 [E,d,h])
  *   dw2[e] = act_e^T . dye_e                                      (dw2 [E,h,d])
- * with H1, H3 from the forward's h13 and act from its act.  Weight gradients
- * are written (not accumulated); experts with no rows get zeros.  The weight
- * gradients have the input dtype (bf16 rounds once from fp32 sums).
+ * with H1, H3 from the forward's h13 and act from its act.
+ * accumulate_dxs != 0: dxs += (one rounding of the sum); 0: overwritten.
+ * grad_dt: dtype of dw1, dw3, dw2 -- the input dtype, or XMOE_F32 with bf16
+ * inputs (the fp32 sums are stored without rounding).  accumulate_dw != 0
+ * adds the sums to the caller's gradients (fp32 only: grad_dt must be
+ * XMOE_F32, else XMOE_ERR_UNSUPPORTED), e.g. over micro-batches; 0 writes
+ * them.  Experts with no rows get zeros (accumulate_dw: unchanged).
  * Same offsets and limits as xmoe_expert_ffn_up.
  */
 xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, const void *w2,
                                 const void *act, const void *h13, const void *dye,
                                 xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                 int64_t rows, int32_t d, int32_t h, void *dh13, void *dxs,
-                                void *dw1, void *dw3, void *dw2, void *stream);
+                                int32_t accumulate_dxs, void *dw1, void *dw3, void *dw2,
+                                xmoe_dtype grad_dt, int32_t accumulate_dw, void *stream);
 
 /*
- * The four products of xmoe_expert_ffn_bwd as separate calls, so that a
- * caller can run the weight gradients on another stream beside the data
- * gradients (same definitions, arguments, limits and results):
+ * The four products of xmoe_expert_ffn_bwd ("5.4 MoE模型在分布式训练中的应用",
+ * section 训练流程, the reverse path; X-MoE article, section 2.1.2, per expert)
+ * as separate calls, so that a caller can run the weight gradients on another
+ * stream beside the data gradients (same definitions, arguments, limits,
+ * flags and results):
  *   _dact : dh13 from dye, w2 and the saved h13       (needs nothing else)
- *   _dx   : dxs from dh13, w1, w3                     (after _dact)
- *   _dw13 : dw1, dw3 from xs and dh13                 (after _dact)
- *   _dw2  : dw2 from act and dye                      (independent of the rest)
+ *   _dx   : dxs from dh13, w1, w3; accumulate as accumulate_dxs  (after _dact)
+ *   _dw13 : dw1, dw3 from xs and dh13; grad_dt, accumulate as above (after _dact)
+ *   _dw2  : dw2 from act and dye; grad_dt, accumulate as above   (independent)
  */
 xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void *h13,
                                      xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                      int64_t rows, int32_t d, int32_t h, void *dh13, void *stream);
 xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3,
                                    xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
-                                   int64_t rows, int32_t d, int32_t h, void *dxs, void *stream);
+                                   int64_t rows, int32_t d, int32_t h, void *dxs, int32_t accumulate,
+                                   void *stream);
 xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtype dtype,
                                      const int32_t *expert_offsets, int32_t E, int64_t rows,
-                                     int32_t d, int32_t h, void *dw1, void *dw3, void *stream);
+                                     int32_t d, int32_t h, void *dw1, void *dw3, xmoe_dtype grad_dt,
+                                     int32_t accumulate, void *stream);
 /*
  * xmoe_expert_ffn_bwd_dw13 with the dispatch gather fused into the loads of
  * xs (X-MoE article, section 2.1.2: the PFT's token_ids name each row's source
@@ -312,13 +335,16 @@ xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtyp
 xmoe_status xmoe_expert_ffn_bwd_dw13_gather(const void *x, const int32_t *token_ids, const void *dh13,
                                             xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                             int64_t T, int64_t rows, int32_t d, int32_t h, void *dw1,
-                                            void *dw3, void *stream);
+                                            void *dw3, xmoe_dtype grad_dt, int32_t accumulate,
+                                            void *stream);
 xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,
                                     const int32_t *expert_offsets, int32_t E, int64_t rows,
-                                    int32_t d, int32_t h, void *dw2, void *stream);
+                                    int32_t d, int32_t h, void *dw2, xmoe_dtype grad_dt,
+                                    int32_t accumulate, void *stream);
 
 /*
- * Backward of the dispatch (the transpose of the gather):
+ * Backward of the dispatch ("5.4 MoE模型在分布式训练中的应用", section 训练流程,
+ * the reverse path; the transpose of the X-MoE article's section 2.1.2 gather):
  *   dx[t] = sum_{j=0..k-1} dxs[slot_to_row[t*k+j]]  (+ dx_add[t])
  * summed in fp32 in slot order, rounded once; no atomics.  dx_add [T,d] may be
  * NULL (the shared experts' input gradient goes here).
@@ -331,8 +357,10 @@ xmoe_status xmoe_dispatch_bwd(const void *dxs, const xmoe_pft *pft, int64_t T, i
 size_t xmoe_route_bwd_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype dtype);
 
 /*
- * Backward of the gate through the probabilities (the top-k selection is
- * piecewise constant and carries no gradient; the biases get none):
+ * Backward of the gate ("5.4 MoE模型在分布式训练中的应用", section 训练流程: the
+ * reverse path reaches the gate's scores) through the probabilities (the top-k
+ * selection is piecewise constant and carries no gradient; the biases get
+ * none):
  *   p = softmax(logits[t]),  g[t,e] = dtopk_w[t,j] if e == topk_ids[t,j] else 0
  *   c_t = sum_j p[t, topk_ids[t,j]] * dtopk_w[t,j]
  *   dz[t,e] = p[t,e] * (g[t,e] - c_t) * inv_temperature

@@ -63,24 +63,28 @@ _lib_pft_ws = _sig("xmoe_build_pft_workspace_size", [_i64, _i32, _i32], _sz)
 _lib_pft = _sig("xmoe_build_pft", [_vp, _vp, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _sz, _vp])
 _lib_dispatch = _sig("xmoe_dispatch", [_vp, ctypes.c_int, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp, _vp])
 _lib_up = _sig("xmoe_expert_ffn_up", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp])
-_lib_down = _sig("xmoe_expert_ffn_down", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+_lib_down = _sig("xmoe_expert_ffn_down", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _i32, _vp])
 _lib_ffn = _sig("xmoe_expert_ffn", [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp,
-                                    _vp, _vp])
+                                    _vp, _i32, _vp])
 _lib_up_g = _sig("xmoe_expert_ffn_up_gather", [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32,
                                                 _vp, _vp, _vp])
 _lib_ffn_g = _sig("xmoe_expert_ffn_gather", [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32,
-                                             _i32, _vp, _vp, _vp, _vp])
+                                             _i32, _vp, _vp, _vp, _i32, _vp])
 _lib_combine = _sig("xmoe_combine", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp])
 _lib_combine_bwd = _sig("xmoe_combine_bwd", [_vp, _vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int,
                                              _vp, _vp, _vp])
 _lib_ffn_bwd = _sig("xmoe_expert_ffn_bwd", [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64,
-                                            _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp])
+                                            _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, ctypes.c_int, _i32, _vp])
 _lib_bwd_dact = _sig("xmoe_expert_ffn_bwd_dact", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
-_lib_bwd_dx = _sig("xmoe_expert_ffn_bwd_dx", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
-_lib_bwd_dw13 = _sig("xmoe_expert_ffn_bwd_dw13", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp])
+_lib_bwd_dx = _sig("xmoe_expert_ffn_bwd_dx", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _i32,
+                                              _vp])
+_lib_bwd_dw13 = _sig("xmoe_expert_ffn_bwd_dw13", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp,
+                                                  ctypes.c_int, _i32, _vp])
 _lib_bwd_dw13_g = _sig("xmoe_expert_ffn_bwd_dw13_gather",
-                       [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, _vp])
-_lib_bwd_dw2 = _sig("xmoe_expert_ffn_bwd_dw2", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+                       [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp, ctypes.c_int, _i32,
+                        _vp])
+_lib_bwd_dw2 = _sig("xmoe_expert_ffn_bwd_dw2", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp,
+                                                ctypes.c_int, _i32, _vp])
 _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64, _i32, _i32, ctypes.c_int, _vp,
                                                _vp, _vp])
 _lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
@@ -127,6 +131,14 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return XMOE_F32
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _grad_dt(*grads: torch.Tensor) -> int:
+    """Weight-gradient dtype of the call: that of the gradient tensors (fp32
+    gradients of bf16 inputs are the unrounded sums)."""
+    if any(g.dtype != grads[0].dtype for g in grads):
+        raise ValueError("the weight gradients must share one dtype")
+    return _dt(grads[0])
 
 
 def _stream(stream) -> int:
@@ -233,26 +245,30 @@ def xmoe_expert_ffn_up_gather(x, token_ids, w1, w3, expert_offsets, act, h13=Non
                      _ptr(act), _ptr(h13), _stream(stream)), "xmoe_expert_ffn_up_gather")
 
 
-def xmoe_expert_ffn_gather(x, token_ids, w1, w3, w2, expert_offsets, act, ye, h13=None, stream=None):
+def xmoe_expert_ffn_gather(x, token_ids, w1, w3, w2, expert_offsets, act, ye, h13=None, accumulate=False,
+                           stream=None):
     T, d = x.shape
     E, _, h = w1.shape
     rows = token_ids.shape[0]
     _check(_lib_ffn_g(_ptr(x), _ptr(token_ids), _ptr(w1), _ptr(w3), _ptr(w2), _dt(x), _ptr(expert_offsets), E, T,
-                      rows, d, h, _ptr(act), _ptr(h13), _ptr(ye), _stream(stream)), "xmoe_expert_ffn_gather")
+                      rows, d, h, _ptr(act), _ptr(h13), _ptr(ye), int(bool(accumulate)), _stream(stream)),
+           "xmoe_expert_ffn_gather")
 
 
-def xmoe_expert_ffn_down(act, w2, expert_offsets, ye, stream=None):
+def xmoe_expert_ffn_down(act, w2, expert_offsets, ye, accumulate=False, stream=None):
+    """accumulate=True: ye += act . W2."""
     rows, h = act.shape
     E, _, d = w2.shape
     _check(_lib_down(_ptr(act), _ptr(w2), _dt(act), _ptr(expert_offsets), E, rows, d, h, _ptr(ye),
-                     _stream(stream)), "xmoe_expert_ffn_down")
+                     int(bool(accumulate)), _stream(stream)), "xmoe_expert_ffn_down")
 
 
-def xmoe_expert_ffn(xs, w1, w3, w2, expert_offsets, act, ye, h13=None, stream=None):
+def xmoe_expert_ffn(xs, w1, w3, w2, expert_offsets, act, ye, h13=None, accumulate=False, stream=None):
+    """accumulate=True: ye += the experts' outputs."""
     rows, d = xs.shape
     E, _, h = w1.shape
     _check(_lib_ffn(_ptr(xs), _ptr(w1), _ptr(w3), _ptr(w2), _dt(xs), _ptr(expert_offsets), E, rows, d, h,
-                    _ptr(act), _ptr(h13), _ptr(ye), _stream(stream)), "xmoe_expert_ffn")
+                    _ptr(act), _ptr(h13), _ptr(ye), int(bool(accumulate)), _stream(stream)), "xmoe_expert_ffn")
 
 
 def xmoe_combine(ye, pft: PFT, T: int, y, y_add=None, stream=None):
@@ -269,12 +285,17 @@ def xmoe_combine_bwd(dy, ye, pft: PFT, dye, dtopk_w, stream=None):
                             _stream(stream)), "xmoe_combine_bwd")
 
 
-def xmoe_expert_ffn_bwd(xs, w1, w3, w2, act, h13, dye, expert_offsets, dh13, dxs, dw1, dw3, dw2, stream=None):
+def xmoe_expert_ffn_bwd(xs, w1, w3, w2, act, h13, dye, expert_offsets, dh13, dxs, dw1, dw3, dw2,
+                        accumulate_dxs=False, accumulate_dw=False, stream=None):
+    """The weight gradients' dtype (dw1/dw3/dw2, one dtype) is grad_dt: fp32
+    tensors with bf16 inputs receive the unrounded sums; accumulate_dw adds to
+    them (fp32 only), accumulate_dxs adds to dxs."""
     rows, d = xs.shape
     E, _, h = w1.shape
     _check(_lib_ffn_bwd(_ptr(xs), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(act), _ptr(h13), _ptr(dye), _dt(xs),
-                        _ptr(expert_offsets), E, rows, d, h, _ptr(dh13), _ptr(dxs), _ptr(dw1), _ptr(dw3),
-                        _ptr(dw2), _stream(stream)), "xmoe_expert_ffn_bwd")
+                        _ptr(expert_offsets), E, rows, d, h, _ptr(dh13), _ptr(dxs), int(bool(accumulate_dxs)),
+                        _ptr(dw1), _ptr(dw3), _ptr(dw2), _grad_dt(dw1, dw3, dw2), int(bool(accumulate_dw)),
+                        _stream(stream)), "xmoe_expert_ffn_bwd")
 
 
 def xmoe_expert_ffn_bwd_dact(dye, w2, h13, expert_offsets, dh13, stream=None):
@@ -284,33 +305,36 @@ def xmoe_expert_ffn_bwd_dact(dye, w2, h13, expert_offsets, dh13, stream=None):
                          _stream(stream)), "xmoe_expert_ffn_bwd_dact")
 
 
-def xmoe_expert_ffn_bwd_dx(dh13, w1, w3, expert_offsets, dxs, stream=None):
+def xmoe_expert_ffn_bwd_dx(dh13, w1, w3, expert_offsets, dxs, accumulate=False, stream=None):
     rows, d = dxs.shape
     E, _, h = w1.shape
     _check(_lib_bwd_dx(_ptr(dh13), _ptr(w1), _ptr(w3), _dt(dh13), _ptr(expert_offsets), E, rows, d, h, _ptr(dxs),
-                       _stream(stream)), "xmoe_expert_ffn_bwd_dx")
+                       int(bool(accumulate)), _stream(stream)), "xmoe_expert_ffn_bwd_dx")
 
 
-def xmoe_expert_ffn_bwd_dw13(xs, dh13, expert_offsets, dw1, dw3, stream=None):
+def xmoe_expert_ffn_bwd_dw13(xs, dh13, expert_offsets, dw1, dw3, accumulate=False, stream=None):
+    """grad_dt = dw1/dw3's dtype; accumulate adds to them (fp32 only)."""
     rows, d = xs.shape
     E, _, h = dw1.shape
     _check(_lib_bwd_dw13(_ptr(xs), _ptr(dh13), _dt(xs), _ptr(expert_offsets), E, rows, d, h, _ptr(dw1), _ptr(dw3),
-                         _stream(stream)), "xmoe_expert_ffn_bwd_dw13")
+                         _grad_dt(dw1, dw3), int(bool(accumulate)), _stream(stream)), "xmoe_expert_ffn_bwd_dw13")
 
 
-def xmoe_expert_ffn_bwd_dw13_gather(x, token_ids, dh13, expert_offsets, dw1, dw3, stream=None):
+def xmoe_expert_ffn_bwd_dw13_gather(x, token_ids, dh13, expert_offsets, dw1, dw3, accumulate=False, stream=None):
     T, d = x.shape
     E, _, h = dw1.shape
     rows = dh13.shape[0]
     _check(_lib_bwd_dw13_g(_ptr(x), _ptr(token_ids), _ptr(dh13), _dt(x), _ptr(expert_offsets), E, T, rows, d, h,
-                           _ptr(dw1), _ptr(dw3), _stream(stream)), "xmoe_expert_ffn_bwd_dw13_gather")
+                           _ptr(dw1), _ptr(dw3), _grad_dt(dw1, dw3), int(bool(accumulate)), _stream(stream)),
+           "xmoe_expert_ffn_bwd_dw13_gather")
 
 
-def xmoe_expert_ffn_bwd_dw2(act, dye, expert_offsets, dw2, stream=None):
+def xmoe_expert_ffn_bwd_dw2(act, dye, expert_offsets, dw2, accumulate=False, stream=None):
+    """grad_dt = dw2's dtype; accumulate adds to it (fp32 only)."""
     rows, h = act.shape
     E, _, d = dw2.shape
     _check(_lib_bwd_dw2(_ptr(act), _ptr(dye), _dt(act), _ptr(expert_offsets), E, rows, d, h, _ptr(dw2),
-                        _stream(stream)), "xmoe_expert_ffn_bwd_dw2")
+                        _grad_dt(dw2), int(bool(accumulate)), _stream(stream)), "xmoe_expert_ffn_bwd_dw2")
 
 
 def xmoe_dispatch_bwd(dxs, pft: PFT, T: int, dx, dx_add=None, stream=None):

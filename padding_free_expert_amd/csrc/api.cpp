@@ -108,6 +108,18 @@ xmoe_status check_ffn_sizes(const int32_t *offsets, int32_t E, int64_t rows, int
     return XMOE_OK;
 }
 
+// Weight-gradient dtype: the input dtype, or fp32 with bf16 inputs (unrounded
+// sums).  Accumulating into the gradients needs fp32 gradients.
+xmoe_status check_grad_dt(xmoe_dtype dtype, xmoe_dtype grad_dt, int32_t accumulate) {
+    if (grad_dt != XMOE_F32 && grad_dt != XMOE_BF16)
+        return fail(XMOE_ERR_UNSUPPORTED, "unknown grad_dt %d", static_cast<int>(grad_dt));
+    if (dtype == XMOE_F32 && grad_dt != XMOE_F32)
+        return fail(XMOE_ERR_UNSUPPORTED, "fp32 inputs need grad_dt = XMOE_F32");
+    if (accumulate && grad_dt != XMOE_F32)
+        return fail(XMOE_ERR_UNSUPPORTED, "accumulating weight gradients needs grad_dt = XMOE_F32");
+    return XMOE_OK;
+}
+
 #define TRY(expr)                         \
     do {                                  \
         xmoe_status _s = (expr);          \
@@ -136,7 +148,7 @@ extern "C" {
 
 const char *xmoe_last_error(void) { return g_err.c_str(); }
 
-int xmoe_version(void) { return 100; }
+int xmoe_version(void) { return 200; }
 
 xmoe_status xmoe_query_device(int ordinal, int *is_gfx950) {
     REQUIRE(is_gfx950, XMOE_ERR_INVALID_VALUE, "is_gfx950 is NULL");
@@ -247,13 +259,15 @@ xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, x
 }
 
 xmoe_status xmoe_expert_ffn_down(const void *act, const void *w2, xmoe_dtype dtype, const int32_t *expert_offsets,
-                                 int32_t E, int64_t rows, int32_t d, int32_t h, void *ye, void *stream) {
+                                 int32_t E, int64_t rows, int32_t d, int32_t h, void *ye, int32_t accumulate,
+                                 void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(w2 && (rows == 0 || (act && ye)), XMOE_ERR_INVALID_VALUE, "act, w2 and ye are required");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     REQUIRE(aligned16(act) && aligned16(w2) && aligned16(ye), XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, S(stream)),
+    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, accumulate != 0,
+                                            S(stream)),
                       "xmoe_expert_ffn_down launch");
 }
 
@@ -276,7 +290,7 @@ xmoe_status xmoe_expert_ffn_up_gather(const void *x, const int32_t *token_ids, c
 xmoe_status xmoe_expert_ffn_gather(const void *x, const int32_t *token_ids, const void *w1, const void *w3,
                                    const void *w2, xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                    int64_t T, int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *ye,
-                                   void *stream) {
+                                   int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(w1 && w3 && w2 && (rows == 0 || (act && ye)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
@@ -287,13 +301,14 @@ xmoe_status xmoe_expert_ffn_gather(const void *x, const int32_t *token_ids, cons
     hipError_t e = xmoe::launch_ffn_up(dtype, x, token_ids, T, w1, w3, expert_offsets, E, rows, d, h, act, h13,
                                        S(stream));
     if (e != hipSuccess) return hip_status(e, "xmoe_expert_ffn_gather up-projection launch");
-    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, S(stream)),
+    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, accumulate != 0,
+                                            S(stream)),
                       "xmoe_expert_ffn_gather down-projection launch");
 }
 
 xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, const void *w2, xmoe_dtype dtype,
                             const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h, void *act,
-                            void *h13, void *ye, void *stream) {
+                            void *h13, void *ye, int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(w1 && w3 && w2 && (rows == 0 || (xs && act && ye)), XMOE_ERR_INVALID_VALUE,
             "a required pointer is NULL");
@@ -304,7 +319,8 @@ xmoe_status xmoe_expert_ffn(const void *xs, const void *w1, const void *w3, cons
     CHECK_DEVICE();
     hipError_t e = xmoe::launch_ffn_up(dtype, xs, nullptr, 0, w1, w3, expert_offsets, E, rows, d, h, act, h13, S(stream));
     if (e != hipSuccess) return hip_status(e, "xmoe_expert_ffn up-projection launch");
-    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, S(stream)),
+    return hip_status(xmoe::launch_ffn_down(dtype, act, w2, expert_offsets, E, rows, d, h, ye, accumulate != 0,
+                                            S(stream)),
                       "xmoe_expert_ffn down-projection launch");
 }
 
@@ -336,9 +352,11 @@ xmoe_status xmoe_combine_bwd(const void *dy, const void *ye, const xmoe_pft *pft
 
 xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
                                 const void *h13, const void *dye, xmoe_dtype dtype, const int32_t *expert_offsets,
-                                int32_t E, int64_t rows, int32_t d, int32_t h, void *dh13, void *dxs, void *dw1,
-                                void *dw3, void *dw2, void *stream) {
+                                int32_t E, int64_t rows, int32_t d, int32_t h, void *dh13, void *dxs,
+                                int32_t accumulate_dxs, void *dw1, void *dw3, void *dw2, xmoe_dtype grad_dt,
+                                int32_t accumulate_dw, void *stream) {
     TRY(check_dtype(dtype));
+    TRY(check_grad_dt(dtype, grad_dt, accumulate_dw));
     REQUIRE(w1 && w3 && w2 && dw1 && dw3 && dw2 && (rows == 0 || (xs && act && h13 && dye && dh13 && dxs)),
             XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
@@ -348,7 +366,8 @@ xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, 
             XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
     CHECK_DEVICE();
     return hip_status(xmoe::launch_ffn_bwd(dtype, xs, w1, w3, w2, act, h13, dye, expert_offsets, E, rows, d, h, dh13,
-                                           dxs, dw1, dw3, dw2, S(stream)),
+                                           dxs, accumulate_dxs != 0, dw1, dw3, dw2, grad_dt, accumulate_dw != 0,
+                                           S(stream)),
                       "xmoe_expert_ffn_bwd launch");
 }
 
@@ -367,35 +386,39 @@ xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void
 
 xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3, xmoe_dtype dtype,
                                    const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
-                                   void *dxs, void *stream) {
+                                   void *dxs, int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
     REQUIRE(w1 && w3 && (rows == 0 || (dh13 && dxs)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     REQUIRE(aligned16(dh13) && aligned16(w1) && aligned16(w3) && aligned16(dxs), XMOE_ERR_UNSUPPORTED,
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_bwd_dx(dtype, dh13, w1, w3, expert_offsets, E, rows, d, h, dxs, S(stream)),
+    return hip_status(xmoe::launch_ffn_bwd_dx(dtype, dh13, w1, w3, expert_offsets, E, rows, d, h, dxs, accumulate != 0,
+                                              S(stream)),
                       "xmoe_expert_ffn_bwd_dx launch");
 }
 
 xmoe_status xmoe_expert_ffn_bwd_dw13(const void *xs, const void *dh13, xmoe_dtype dtype,
                                      const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
-                                     void *dw1, void *dw3, void *stream) {
+                                     void *dw1, void *dw3, xmoe_dtype grad_dt, int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
+    TRY(check_grad_dt(dtype, grad_dt, accumulate));
     REQUIRE(dw1 && dw3 && (rows == 0 || (xs && dh13)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     REQUIRE(aligned16(xs) && aligned16(dh13) && aligned16(dw1) && aligned16(dw3), XMOE_ERR_UNSUPPORTED,
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
     return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, xs, nullptr, 0, dh13, expert_offsets, E, rows, d, h, dw1, dw3,
-                                                S(stream)),
+                                                grad_dt, accumulate != 0, S(stream)),
                       "xmoe_expert_ffn_bwd_dw13 launch");
 }
 
 xmoe_status xmoe_expert_ffn_bwd_dw13_gather(const void *x, const int32_t *token_ids, const void *dh13,
                                             xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E, int64_t T,
-                                            int64_t rows, int32_t d, int32_t h, void *dw1, void *dw3, void *stream) {
+                                            int64_t rows, int32_t d, int32_t h, void *dw1, void *dw3,
+                                            xmoe_dtype grad_dt, int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
+    TRY(check_grad_dt(dtype, grad_dt, accumulate));
     REQUIRE(dw1 && dw3 && (rows == 0 || dh13), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     TRY(check_gather(x, token_ids, T, rows, d, dtype));
@@ -403,20 +426,22 @@ xmoe_status xmoe_expert_ffn_bwd_dw13_gather(const void *x, const int32_t *token_
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
     return hip_status(xmoe::launch_ffn_bwd_dw13(dtype, x, token_ids, T, dh13, expert_offsets, E, rows, d, h, dw1, dw3,
-                                                S(stream)),
+                                                grad_dt, accumulate != 0, S(stream)),
                       "xmoe_expert_ffn_bwd_dw13_gather launch");
 }
 
 xmoe_status xmoe_expert_ffn_bwd_dw2(const void *act, const void *dye, xmoe_dtype dtype,
                                     const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h,
-                                    void *dw2, void *stream) {
+                                    void *dw2, xmoe_dtype grad_dt, int32_t accumulate, void *stream) {
     TRY(check_dtype(dtype));
+    TRY(check_grad_dt(dtype, grad_dt, accumulate));
     REQUIRE(dw2 && (rows == 0 || (act && dye)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     REQUIRE(aligned16(act) && aligned16(dye) && aligned16(dw2), XMOE_ERR_UNSUPPORTED,
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_bwd_dw2(dtype, act, dye, expert_offsets, E, rows, d, h, dw2, S(stream)),
+    return hip_status(xmoe::launch_ffn_bwd_dw2(dtype, act, dye, expert_offsets, E, rows, d, h, dw2, grad_dt,
+                                               accumulate != 0, S(stream)),
                       "xmoe_expert_ffn_bwd_dw2 launch");
 }
 

@@ -68,6 +68,14 @@ bool large_tiles_filled(int64_t rows, int E, int64_t n, int bn) {
     return per_group >= 256 && r >= 96 && static_cast<double>(r) + 2.0 * sd <= 256.0;
 }
 
+// A k-split product (weight gradients) has E x ceil(m/bm) x ceil(n/bm) tiles
+// whatever the rows.  The 256-square tile runs one block per compute unit, so
+// its grid fills the device from 256 tiles (the DeepSeek-MoE-16B dW2 has 384;
+// one dense group of h = 2048, d = 4096 has 128 and keeps the smaller tile).
+bool ksplit_fills(int E, int64_t m, int64_t n, int bm) {
+    return static_cast<int64_t>(E) * ((m + bm - 1) / bm) * ((n + bm - 1) / bm) >= 256;
+}
+
 GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
     GemmArgs p{};
     p.group_mode = GM_KSPLIT;
@@ -114,7 +122,7 @@ hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t
 }
 
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows, int d,
-                           int h, void *ye, hipStream_t s) {
+                           int h, void *ye, bool accumulate, hipStream_t s) {
     GemmArgs p = rows_args(offsets, E, rows);
     p.N = d;
     p.K = h;
@@ -125,7 +133,11 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
     p.b_gstride = static_cast<int64_t>(h) * d;
     p.C0 = ye;
     p.ldc = d;
+    p.accum = accumulate ? 1 : 0;
     if (dt != kBF16) return launch_gemm_f32<1, true, false, EPI_STORE>(p, s);
+    // ye += act . W2: the staged read-modify-write epilogue (one rounding of
+    // ye + products), on the tile that serves every size
+    if (accumulate) return launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_ACCUM, bf16_t, 2>(p, s);
     return large_tiles_filled(rows, E, d, 256)
                ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, false, 4, EPI_STORE, bf16_t, 1>(p, s)
                : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
@@ -163,7 +175,7 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
 
 // dxs = dH1 . W1[e]^T + dH3 . W3[e]^T
 hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
-                             int64_t rows, int d, int h, void *dxs, hipStream_t s) {
+                             int64_t rows, int d, int h, void *dxs, bool accumulate, hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     const size_t esz = dt == kBF16 ? 2 : 4;
     hipError_t err;
@@ -180,10 +192,13 @@ hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const voi
     p.b_gstride = dh;
     p.C0 = dxs;
     p.ldc = d;
+    p.accum = accumulate ? 1 : 0;
     // one 256x256 tile of eight waves per compute unit at every size (measured
-    // level with or ahead of four waves from 256 to 1638 rows per expert)
+    // level with or ahead of four waves from 256 to 1638 rows per expert);
+    // dxs += ...: the staged read-modify-write epilogue
     err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_STORE>(p, s)
-                      : launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
+          : accumulate ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_ACCUM, bf16_t, 1>(p, s)
+                       : launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_STORE, bf16_t, 1>(p, s);
     return err;
 }
 
@@ -191,7 +206,7 @@ hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const voi
 // with row_map, xs[r] is read as xs[row_map[r]] (xs then has map_rows rows)
 hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *dh13,
                                const int32_t *offsets, int E, int64_t rows, int d, int h, void *dw1, void *dw3,
-                               hipStream_t s) {
+                               int grad_dt, bool accumulate, hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     const size_t esz = dt == kBF16 ? 2 : 4;
     hipError_t err;
@@ -209,10 +224,17 @@ hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, i
     p.c_gstride = dh;
     p.a_map = row_map;  // the gather fused into the A loads: k row r reads xs[row_map[r]]
     p.a_map_rows = map_rows;
+    p.accum = accumulate ? 1 : 0;   // fp32 gradients only
     // short reductions (few rows per expert) leave each tile little work to
     // hide its pipeline fill and epilogue behind: three blocks per compute unit
     // (two-slot rings) overlap more of them
     if (dt != kBF16) return launch_gemm_f32<2, false, false, EPI_STORE>(p, s);
+    if (grad_dt != kBF16) {
+        // fp32 gradients of bf16 inputs: the sums leave unrounded (stored, or
+        // added to the caller's fp32 gradients), one tile at every size
+        return row_map ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, float, 2, true>(p, s)
+                       : launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 3, EPI_STORE, float, 2>(p, s);
+    }
     const bool short_k = rows / (E > 0 ? E : 1) < 1024;
     if (row_map)
         err = short_k ? launch_gemm_dma<128, 128, 32, 2, 2, 2, false, false, 2, EPI_STORE, bf16_t, 3, true>(p, s)
@@ -225,7 +247,7 @@ hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, i
 
 // dW2[e] = act_e^T . dye_e
 hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const int32_t *offsets, int E, int64_t rows,
-                              int d, int h, void *dw2, hipStream_t s) {
+                              int d, int h, void *dw2, int grad_dt, bool accumulate, hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     hipError_t err;
     GemmArgs p = ksplit_args(offsets, E, rows);
@@ -238,22 +260,28 @@ hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const in
     p.C0 = dw2;
     p.ldc = d;
     p.c_gstride = dh;
+    p.accum = accumulate ? 1 : 0;   // fp32 gradients only
+    if (dt != kBF16) return launch_gemm_f32<1, false, false, EPI_STORE>(p, s);
+    if (grad_dt != kBF16)
+        return launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, float, 2>(p, s);
     // the 256-row tile whenever its grid fills the device: at 384 rows per
     // expert (DeepSeek-MoE-16B shape) it made the whole step 0.8% faster than
-    // the 128-row tile (A/B, three alternations)
-    err = dt != kBF16 ? launch_gemm_f32<1, false, false, EPI_STORE>(p, s)
-          : large_grid(rows, E, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, false, false, 4, EPI_STORE, bf16_t, 1>(p, s)
-                                         : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
+    // the 128-row tile (A/B, three alternations).  The grid of this k-split
+    // product is E x ceil(h/256) x ceil(d/256) tiles, whatever the rows.
+    err = ksplit_fills(E, h, d, 256) ? launch_gemm_dma<256, 256, 32, 4, 2, 1, false, false, 4, EPI_STORE, bf16_t, 1>(p, s)
+                                      : launch_gemm_dma<128, 256, 32, 2, 2, 1, false, false, 3, EPI_STORE, bf16_t, 2>(p, s);
     return err;
 }
 
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
                           const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d, int h,
-                          void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s) {
+                          void *dh13, void *dxs, bool accumulate_dxs, void *dw1, void *dw3, void *dw2, int grad_dt,
+                          bool accumulate_dw, hipStream_t s) {
     hipError_t err = launch_ffn_bwd_dact(dt, dye, w2, h13, offsets, E, rows, d, h, dh13, s);
-    if (err == hipSuccess) err = launch_ffn_bwd_dx(dt, dh13, w1, w3, offsets, E, rows, d, h, dxs, s);
-    if (err == hipSuccess) err = launch_ffn_bwd_dw13(dt, xs, nullptr, 0, dh13, offsets, E, rows, d, h, dw1, dw3, s);
-    if (err == hipSuccess) err = launch_ffn_bwd_dw2(dt, act, dye, offsets, E, rows, d, h, dw2, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dx(dt, dh13, w1, w3, offsets, E, rows, d, h, dxs, accumulate_dxs, s);
+    if (err == hipSuccess)
+        err = launch_ffn_bwd_dw13(dt, xs, nullptr, 0, dh13, offsets, E, rows, d, h, dw1, dw3, grad_dt, accumulate_dw, s);
+    if (err == hipSuccess) err = launch_ffn_bwd_dw2(dt, act, dye, offsets, E, rows, d, h, dw2, grad_dt, accumulate_dw, s);
     return err;
 }
 

@@ -63,6 +63,9 @@ struct GemmArgs {
     // (partial sums, EPI_STORE); kparts <= 1 means no split.
     int kparts;
     int kpart_len;
+    // fp32 outputs with EPI_STORE: nonzero adds the products to C (C0 and Cx)
+    // instead of overwriting it (one fp32 addition per element)
+    int accum;
 };
 
 // ---------------------------------------------------------------- epilogues
@@ -75,8 +78,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, int64_t cbase_row, i
     // cbase_row: first C row of the group (GM_ROWS) ; cbase_off: group offset (GM_KSPLIT)
     const int64_t row = cbase_row + m;
     if constexpr (EPI == EPI_STORE) {
-        Elem<OutT>::store(static_cast<OutT *>(p.C0), cbase_off + row * p.ldc + n, v0);
-        if (p.Cx) Elem<OutT>::store(static_cast<OutT *>(p.Cx), cbase_off + row * p.ldc + n, v1);
+        const int64_t i = cbase_off + row * p.ldc + n;
+        if (std::is_same<OutT, float>::value && p.accum) {
+            OutT *c0 = static_cast<OutT *>(p.C0);
+            Elem<OutT>::store(c0, i, Elem<OutT>::load(c0, i) + v0);
+            if (p.Cx) {
+                OutT *cx = static_cast<OutT *>(p.Cx);
+                Elem<OutT>::store(cx, i, Elem<OutT>::load(cx, i) + v1);
+            }
+        } else {
+            Elem<OutT>::store(static_cast<OutT *>(p.C0), i, v0);
+            if (p.Cx) Elem<OutT>::store(static_cast<OutT *>(p.Cx), i, v1);
+        }
     } else if constexpr (EPI == EPI_ACCUM) {
         OutT *c = static_cast<OutT *>(p.C0);
         const int64_t i = cbase_off + row * p.ldc + n;
@@ -301,6 +314,16 @@ __device__ __forceinline__ void epilogue4(const GemmArgs &p, int64_t crow, int64
             float4 o = *reinterpret_cast<float4 *>(c);
             o.x += v0[0]; o.y += v0[1]; o.z += v0[2]; o.w += v0[3];
             *reinterpret_cast<float4 *>(c) = o;
+        } else if (p.accum) {
+            float4 o = *reinterpret_cast<float4 *>(c);
+            o.x += v0[0]; o.y += v0[1]; o.z += v0[2]; o.w += v0[3];
+            *reinterpret_cast<float4 *>(c) = o;
+            if (p.Cx) {
+                float4 *cx = reinterpret_cast<float4 *>(static_cast<float *>(p.Cx) + coff + row * p.ldc + n);
+                float4 u = *cx;
+                u.x += v1[0]; u.y += v1[1]; u.z += v1[2]; u.w += v1[3];
+                *cx = u;
+            }
         } else {
             *reinterpret_cast<float4 *>(c) = make_float4(v0[0], v0[1], v0[2], v0[3]);
             if (p.Cx)

@@ -66,21 +66,25 @@ hipError_t launch_combine_bwd(int dt, const void *dy, const void *ye, const int3
 hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *w1,
                          const void *w3, const int32_t *offsets, int E, int64_t rows, int d, int h, void *act,
                          void *h13, hipStream_t s);
+// accumulate: ye += act . W2 (else ye =)
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows,
-                           int d, int h, void *ye, hipStream_t s);
+                           int d, int h, void *ye, bool accumulate, hipStream_t s);
 // the four products of the expert backward, each on its own stream if the caller wants
 hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const void *h13, const int32_t *offsets, int E,
                                int64_t rows, int d, int h, void *dh13, hipStream_t s);
 hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
-                             int64_t rows, int d, int h, void *dxs, hipStream_t s);
+                             int64_t rows, int d, int h, void *dxs, bool accumulate, hipStream_t s);
 // row_map (may be nullptr): k row r of an expert reads xs[row_map[r]] (xs has map_rows rows)
+// grad_dt: dtype of the weight gradients (kF32 with bf16 inputs: unrounded
+// sums); accumulate (fp32 gradients only): dW += the sums
 hipError_t launch_ffn_bwd_dw13(int dt, const void *xs, const int32_t *row_map, int64_t map_rows, const void *dh13,
                                const int32_t *offsets, int E, int64_t rows, int d, int h, void *dw1, void *dw3,
-                               hipStream_t s);
+                               int grad_dt, bool accumulate, hipStream_t s);
 hipError_t launch_ffn_bwd_dw2(int dt, const void *act, const void *dye, const int32_t *offsets, int E, int64_t rows,
-                              int d, int h, void *dw2, hipStream_t s);
+                              int d, int h, void *dw2, int grad_dt, bool accumulate, hipStream_t s);
 hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3, const void *w2, const void *act,
                           const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d,
-                          int h, void *dh13, void *dxs, void *dw1, void *dw3, void *dw2, hipStream_t s);
+                          int h, void *dh13, void *dxs, bool accumulate_dxs, void *dw1, void *dw3, void *dw2,
+                          int grad_dt, bool accumulate_dw, hipStream_t s);
 
 }  // namespace xmoe

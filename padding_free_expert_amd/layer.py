@@ -38,8 +38,9 @@ class PaddingFreeMoE:
     h (and merge_shared), the shared experts become that many more experts that
     every token is routed to with weight 1: one buffer, one call per product
     for routed and shared experts together.  The layer then keeps the routed
-    and shared weights in one [E + n, d, h] / [E + n, h, d] buffer (copied at
-    construction).  Otherwise (the default) the shared FFN runs as a separate
+    and shared weights in one [E + n, d, h] / [E + n, h, d] buffer, copied at
+    construction and again by refresh_weights() (call it after changing the
+    weights).  Otherwise (the default) the shared FFN runs as a separate
     FFN of its own width on a second stream beside the routed path.  Measured
     on the DeepSeek-MoE-16B shape the separate stream is ~2.7% faster: it fills
     the routed products' tails, and the merged buffer's mean rows per expert
@@ -72,12 +73,10 @@ class PaddingFreeMoE:
         R = T * kc
         self.R = R
         if self.merged:
-            ns = self.ns
-            s1 = weights["s1"].view(d, ns, h).permute(1, 0, 2)
-            s3 = weights["s3"].view(d, ns, h).permute(1, 0, 2)
-            self.W1 = torch.cat([w1, s1]).contiguous()
-            self.W3 = torch.cat([weights["w3"], s3]).contiguous()
-            self.W2 = torch.cat([weights["w2"], weights["s2"].view(ns, h, d)]).contiguous()
+            self.W1 = torch.empty((Ec, d, h), dtype=dt, device=dev)
+            self.W3 = torch.empty((Ec, d, h), dtype=dt, device=dev)
+            self.W2 = torch.empty((Ec, h, d), dtype=dt, device=dev)
+            self.refresh_weights()
         else:
             self.W1, self.W3, self.W2 = w1, weights["w3"], weights["w2"]
         self.wside = torch.cuda.Stream(device=dev) if backward else None
@@ -121,6 +120,26 @@ class PaddingFreeMoE:
                 self._ds1 = torch.empty((1, d, hs), dtype=dt, device=dev)
                 self._ds3 = torch.empty((1, d, hs), dtype=dt, device=dev)
                 self._ds2 = torch.empty((1, hs, d), dtype=dt, device=dev)
+
+    def refresh_weights(self, stream=None) -> None:
+        """Merged layout only: copy the routed and shared weights (the tensors in
+        the weights dict, in their own layouts) into the layer's [E + n, ...]
+        buffers, in place on `stream`.  The merged buffers are copies, so a
+        caller that updates the weights (an optimizer step) calls this before
+        the next forward; without merging the layer reads the caller's tensors
+        directly and this does nothing.  It allocates nothing, so it can sit
+        inside a captured graph."""
+        if not self.merged:
+            return
+        w, E, ns, d, h = self.w, self.E, self.ns, self.d, self.h
+        main = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(main):
+            self.W1[:E].copy_(w["w1"])
+            self.W3[:E].copy_(w["w3"])
+            self.W2[:E].copy_(w["w2"])
+            self.W1[E:].copy_(w["s1"].view(d, ns, h).permute(1, 0, 2))
+            self.W3[E:].copy_(w["s3"].view(d, ns, h).permute(1, 0, 2))
+            self.W2[E:].copy_(w["s2"].view(ns, h, d))
 
     # views of the unmerged shared-expert weights as a single expert of width n*h_s
     def _shared_w(self):

@@ -106,13 +106,33 @@ def test_gathered_wgrad_rejects_on_host(xm):
     p = ctypes.c_void_p(16)  # never dereferenced
     f = xm._lib_bwd_dw13_g
     # x [T, d] of 2^31 bytes or more cannot be gathered through one buffer
-    assert f(p, p, p, 1, p, 4, 1 << 17, 100, 8192, 64, p, p, None) == 2
+    assert f(p, p, p, 1, p, 4, 1 << 17, 100, 8192, 64, p, p, 1, 0, None) == 2
     # NULL x or token_ids with rows to gather; NULL dh13
-    assert f(None, p, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
-    assert f(p, None, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
-    assert f(p, p, None, 1, p, 4, 100, 100, 64, 64, p, p, None) == 1
+    assert f(None, p, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
+    assert f(p, None, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
+    assert f(p, p, None, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
     # T < 1, h not a multiple of 8, misaligned x
-    assert f(p, p, p, 1, p, 4, 0, 100, 64, 64, p, p, None) == 1
-    assert f(p, p, p, 1, p, 4, 100, 100, 64, 12, p, p, None) == 2
-    assert f(ctypes.c_void_p(18), p, p, 1, p, 4, 100, 100, 64, 64, p, p, None) == 2
+    assert f(p, p, p, 1, p, 4, 0, 100, 64, 64, p, p, 1, 0, None) == 1
+    assert f(p, p, p, 1, p, 4, 100, 100, 64, 12, p, p, 1, 0, None) == 2
+    assert f(ctypes.c_void_p(18), p, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 2
     assert xm._lib_last_error() != b""
+
+
+def test_weight_gradient_dtype_and_accumulate_rejected_on_host(xm):
+    """grad_dt: the input dtype, or fp32 with bf16 inputs; accumulating into the
+    weight gradients needs fp32 gradients."""
+    p = ctypes.c_void_p(16)  # never dereferenced
+    BF16, F32 = 1, 0
+    dw2 = xm._lib_bwd_dw2
+    assert dw2(p, p, BF16, p, 4, 100, 64, 64, p, 7, 0, None) == 2           # unknown grad_dt
+    assert dw2(p, p, F32, p, 4, 100, 64, 64, p, BF16, 0, None) == 2        # fp32 inputs, bf16 gradients
+    assert dw2(p, p, BF16, p, 4, 100, 64, 64, p, BF16, 1, None) == 2       # accumulate into bf16
+    assert b"grad_dt" in xm._lib_last_error()
+    dw13 = xm._lib_bwd_dw13
+    assert dw13(p, p, BF16, p, 4, 100, 64, 64, p, p, BF16, 1, None) == 2
+    assert xm._lib_bwd_dw13_g(p, p, p, BF16, p, 4, 100, 100, 64, 64, p, p, BF16, 1, None) == 2
+    bwd = xm._lib_ffn_bwd
+    assert bwd(p, p, p, p, p, p, p, BF16, p, 4, 100, 64, 64, p, p, 0, p, p, p, BF16, 1, None) == 2
+    assert bwd(p, p, p, p, p, p, p, F32, p, 4, 100, 64, 64, p, p, 0, p, p, p, BF16, 0, None) == 2
+    assert xm.xmoe_version() == 200
+
