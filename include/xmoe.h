@@ -149,6 +149,24 @@ xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t
                            void *stream);
 
 /*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: xmoe_build_pft
+ * with no workspace argument.  The three kernels use the library's own static
+ * scratch of xmoe_build_pft_noalloc_max_bytes() bytes (4 MiB) instead, one copy
+ * per device, held until the process ends; the call allocates and frees
+ * nothing and leaves no state the next call depends on (every count it reads
+ * it has written first).  Calls that overlap on one device (two streams, or two
+ * host threads) share that scratch and race: serialise them.  Sizes needing
+ * more scratch than that (xmoe_build_pft_workspace_size(T, E, k) above the
+ * maximum; at E = 1024 that is beyond 130816 tokens) return XMOE_ERR_UNSUPPORTED
+ * before anything is launched.  Otherwise the same arguments, limits and
+ * results, bit for bit, as xmoe_build_pft.
+ */
+size_t xmoe_build_pft_noalloc_max_bytes(void);
+xmoe_status xmoe_build_pft_noalloc(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E,
+                                   int32_t k, const xmoe_pft *pft, void *stream);
+
+/*
  * The same buffer with shared experts carried as experts every token is
  * routed to with weight 1 (the shared expert beside the routed ones of
  * "5.4 MoE模型在分布式训练中的应用", section 实际案例, held in the X-MoE

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "XmoeError", "PFT", "lib_path", "xmoe_version", "xmoe_query_device", "xmoe_route",
     "xmoe_route_workspace_size",
-    "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_build_pft_shared", "xmoe_dispatch", "xmoe_expert_ffn_up",
+    "xmoe_build_pft_workspace_size", "xmoe_build_pft", "xmoe_build_pft_noalloc", "xmoe_build_pft_noalloc_max_bytes",
+    "xmoe_build_pft_shared", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
     "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13", "xmoe_expert_ffn_bwd_dw13_gather",
@@ -90,6 +91,8 @@ _lib_dispatch_bwd = _sig("xmoe_dispatch_bwd", [_vp, ctypes.POINTER(_CPft), _i64,
 _lib_rbwd_ws = _sig("xmoe_route_bwd_workspace_size", [_i64, _i32, _i32, ctypes.c_int], _sz)
 _lib_rbwd = _sig("xmoe_route_bwd", [_vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int, _i64, _i32, _i32, _i32, _f32,
                                     _i32, _vp, _vp, _vp, _sz, _vp])
+_lib_pft_na = _sig("xmoe_build_pft_noalloc", [_vp, _vp, _i64, _i32, _i32, ctypes.POINTER(_CPft), _vp])
+_lib_pft_na_max = _sig("xmoe_build_pft_noalloc_max_bytes", [], _sz)
 _lib_pft_sh = _sig("xmoe_build_pft_shared", [_vp, _vp, _i64, _i32, _i32, _i32, ctypes.POINTER(_CPft), _vp, _sz, _vp])
 _lib_pilots_ws = _sig("xmoe_build_pilots_workspace_size", [_i64, _i32, _i32, _i32], _sz)
 _lib_pilots = _sig("xmoe_build_pilots", [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
@@ -210,6 +213,19 @@ def xmoe_build_pft(topk_ids, topk_w, E: int, pft: PFT, workspace, stream=None):
     c = pft.c()
     _check(_lib_pft(_ptr(topk_ids), _ptr(topk_w), T, E, k, ctypes.byref(c), _ptr(workspace),
                     workspace.numel() * workspace.element_size(), _stream(stream)), "xmoe_build_pft")
+
+
+def xmoe_build_pft_noalloc(topk_ids, topk_w, E: int, pft: PFT, stream=None):
+    """xmoe_build_pft on the library's static scratch: no workspace, nothing
+    allocated (calls overlapping on one device race)."""
+    T, k = topk_ids.shape
+    c = pft.c()
+    _check(_lib_pft_na(_ptr(topk_ids), _ptr(topk_w), T, E, k, ctypes.byref(c), _stream(stream)),
+           "xmoe_build_pft_noalloc")
+
+
+def xmoe_build_pft_noalloc_max_bytes() -> int:
+    return int(_lib_pft_na_max())
 
 
 def xmoe_build_pft_shared(topk_ids, topk_w, E_routed: int, n_shared: int, pft: PFT, workspace, stream=None):

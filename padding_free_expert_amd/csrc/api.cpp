@@ -211,6 +211,27 @@ xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t
                       "xmoe_build_pft launch");
 }
 
+size_t xmoe_build_pft_noalloc_max_bytes(void) { return xmoe::kPftScratchBytes; }
+
+xmoe_status xmoe_build_pft_noalloc(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E, int32_t k,
+                                   const xmoe_pft *pft, void *stream) {
+    REQUIRE(T == 0 || (topk_ids && topk_w), XMOE_ERR_INVALID_VALUE, "topk_ids and topk_w are required");
+    REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
+    REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
+    REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
+    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    TRY(check_pft(pft, T > 0, T > 0, T > 0));
+    REQUIRE(pft->tokens_per_expert && pft->expert_offsets, XMOE_ERR_INVALID_VALUE,
+            "pft->tokens_per_expert and pft->expert_offsets are required");
+    REQUIRE(xmoe::pft_workspace(T, E) <= xmoe::kPftScratchBytes, XMOE_ERR_UNSUPPORTED,
+            "T and E need %zu bytes of scratch, more than the %zu the library holds per device "
+            "(use xmoe_build_pft with a workspace)",
+            xmoe::pft_workspace(T, E), xmoe::kPftScratchBytes);
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_build_pft_static(topk_ids, topk_w, T, E, k, to_ptrs(pft), S(stream)),
+                      "xmoe_build_pft_noalloc launch");
+}
+
 xmoe_status xmoe_build_pft_shared(const int32_t *topk_ids, const float *topk_w, int64_t T, int32_t E_routed,
                                   int32_t k, int32_t n_shared, const xmoe_pft *pft, void *workspace, size_t ws_bytes,
                                   void *stream) {

@@ -34,6 +34,13 @@ size_t pft_workspace(int64_t T, int E);
 hipError_t launch_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k, int n_always,
                             const PftPtrs &pft, void *ws, hipStream_t s);
 
+// The same build with the library's own static scratch (kPftScratchBytes on
+// each device) in place of a workspace: for callers that cannot allocate.
+// hipErrorInvalidValue when pft_workspace(T, E) exceeds the scratch.
+constexpr size_t kPftScratchBytes = size_t(4) << 20;
+hipError_t launch_build_pft_static(const int32_t *topk_ids, const float *topk_w, int64_t T, int E, int k,
+                                   const PftPtrs &pft, hipStream_t s);
+
 // pilot tokens (Redundancy-Bypassing Dispatch, stage 1); workspace pft_workspace(T, E / experts_per_node)
 struct PilotPtrs {
     int32_t *pilot_token_ids, *pilot_node_ids, *node_counts, *node_offsets, *slot_to_pilot;

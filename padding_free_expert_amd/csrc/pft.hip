@@ -29,10 +29,20 @@
 // Shared experts can ride in the same buffer as experts every token is routed
 // to with weight 1: with n_always > 0 each token has, after its k routed slots,
 // n_always more slots for the last n_always experts (E - n_always + i).
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace xmoe {
+
+// Library-owned scratch for callers that cannot allocate (launch_build_pft_static):
+// the per-block counts and bases of the three kernels below.  Each device that
+// runs the library holds one copy until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host the name is a stand-in, not
+// a device address): it looks up the device address once per device with
+// hipGetSymbolAddress and passes that.
+static __device__ __align__(256) char scratch[kPftScratchBytes];
 
 namespace {
 
@@ -214,6 +224,39 @@ hipError_t launch_build_pft(const int32_t *ids, const float *w, int64_t T, int E
                             const PftPtrs &pft, void *ws, hipStream_t s) {
     return keyed_sort<false>(ids, w, T, E, k, n_always, 1, pft.token_ids, pft.expert_ids, pft.tokens_per_expert, pft.expert_offsets,
                       pft.combine_weights, pft.slot_to_row, ws, s);
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void *g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t pft_scratch_address(void **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // first call on this device (it is current): the device address of its copy
+        void *ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_build_pft_static(const int32_t *ids, const float *w, int64_t T, int E, int k,
+                                   const PftPtrs &pft, hipStream_t s) {
+    if (pft_workspace(T, E) > kPftScratchBytes) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    hipError_t err = pft_scratch_address(&ws);
+    if (err != hipSuccess) return err;
+    // the kernels write every count and base before reading it: nothing to clear
+    return launch_build_pft(ids, w, T, E, k, 0, pft, ws, s);
 }
 
 hipError_t launch_build_pilots(const int32_t *ids, int64_t T, int E, int k, int experts_per_node,

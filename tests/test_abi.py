@@ -136,3 +136,18 @@ def test_weight_gradient_dtype_and_accumulate_rejected_on_host(xm):
     assert bwd(p, p, p, p, p, p, p, F32, p, 4, 100, 64, 64, p, p, 0, p, p, p, BF16, 0, None) == 2
     assert xm.xmoe_version() == 200
 
+
+def test_noalloc_pft_build_limit_on_host(xm):
+    """The allocation-free PFT build takes at most its static scratch
+    (4 MiB: 511 blocks of 256 tokens at 1024 experts) and rejects larger sizes
+    before any launch."""
+    p = ctypes.c_void_p(16)  # never dereferenced
+    pft = xm._CPft(16, 16, 16, 16, 16, 16)
+    mx = xm.xmoe_build_pft_noalloc_max_bytes()
+    assert mx == 4 << 20
+    assert xm.xmoe_build_pft_workspace_size(130816, 1024, 8) <= mx
+    assert xm.xmoe_build_pft_workspace_size(130817, 1024, 8) > mx
+    assert xm._lib_pft_na(p, p, 130817, 1024, 8, ctypes.byref(pft), None) == 2
+    assert b"scratch" in xm._lib_last_error()
+    assert xm._lib_pft_na(p, p, 100, 64, 65, ctypes.byref(pft), None) == 1      # k > E
+    assert xm._lib_pft_na(None, p, 100, 64, 6, ctypes.byref(pft), None) == 1
