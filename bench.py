@@ -81,6 +81,8 @@ def parse():
                     help="recompute H1/H3 in the backward instead of keeping them from the forward")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: pick for ~10-30 s)")
+    ap.add_argument("--cpu-full", type=int, default=0,
+                    help="also time the oracle on the whole workload this many times (median; minutes per run)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale hardware byte counters)")
     ap.add_argument("--timed-only", action="store_true",
@@ -289,11 +291,97 @@ def main():
         print(json.dumps(out), flush=True)
         return
     out["step_ms_cache_flushed"] = pctl(flushed)
+    out["value_cache_flushed"] = round(flops["total"] / (out["step_ms_cache_flushed"]["median"] * 1e-3) / 1e12, 2)
     out["breakdown_ms_serial"] = {k: round(v, 4) for k, v in breakdown.items()}
+    roofline["per_product"] = per_product(xm, wl, layer, weights, x, dy, stream)
     out["ep_rbd"] = ep_rbd(xm, wl, layer, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"], out["parity"] = cpu_baseline(wl, inp, args.cpu_sample_tokens, layer)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(wl, inp, args.cpu_sample_tokens, layer, args.cpu_full)
     print(json.dumps(out), flush=True)
+
+
+def per_product(xm, wl, layer, weights, x, dy, stream, reps=20):
+    """Every product of the step alone: 3 untimed calls, then `reps` calls back
+    to back between two events, on the layer's own buffers (after the timed
+    steps, so they hold one step's values).  Matrix-core products report
+    TFLOP/s against the bf16 peak; the row kernels, the router and its
+    backward report algorithmic GB/s against HBM (each input read once, each
+    output written once), the PFT build microseconds."""
+    import torch
+
+    T, d, E, h, k = wl.T, wl.d, wl.E, wl.h, wl.k
+    R, Ec, off, pft = layer.R, layer.Ec, layer.pft.expert_offsets, layer.pft
+    kc = layer.kc
+    rows = {}
+
+    def run(name, fn, flop=None, nbytes=None):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        r = {"ms": round(ms, 5)}
+        if flop is not None:
+            tf = flop / (ms * 1e-3) / 1e12
+            r.update(gflop=round(flop / 1e9, 2), tflops=round(tf, 1), frac=round(tf / PEAK_BF16_TFLOPS, 4))
+        if nbytes is not None:
+            gb = nbytes / (ms * 1e-3) / 1e9
+            r.update(mbytes=round(nbytes / 1e6, 1), GBps=round(gb, 1), frac_hbm=round(gb / PEAK_HBM_GBS, 4))
+        rows[name] = r
+
+    w = layer.w
+    s = 2  # bytes per bf16 element
+    run("route", lambda: xm.xmoe_route(x, w["wg"], k, layer.topk_ids, layer.topk_w, layer.logits, layer.inv_tau,
+                                       w.get("logit_bias"), w.get("select_bias"), workspace=layer.route_ws),
+        flop=2.0 * T * d * E, nbytes=T * d * s + d * E * s + 4.0 * T * E + 8.0 * T * k)
+    if layer.merged:
+        run("build_pft", lambda: xm.xmoe_build_pft_shared(layer.topk_ids, layer.topk_w, E, layer.ns, pft,
+                                                          layer.pft_ws))
+    else:
+        run("build_pft", lambda: xm.xmoe_build_pft(layer.topk_ids, layer.topk_w, E, pft, layer.pft_ws))
+    h13 = layer.h13
+    run("up", lambda: xm.xmoe_expert_ffn_up_gather(x, pft.token_ids, layer.W1, layer.W3, off, layer.act, h13),
+        flop=4.0 * R * d * h)
+    run("down", lambda: xm.xmoe_expert_ffn_down(layer.act, layer.W2, off, layer.ye), flop=2.0 * R * d * h)
+    y_add = layer.sh_y if layer.side_shared else None
+    run("combine", lambda: xm.xmoe_combine(layer.ye, pft, T, layer.y, y_add=y_add),
+        nbytes=R * d * s + T * d * s * (2 if y_add is not None else 1) + 8.0 * R)
+    if layer.side_shared:
+        hs, so = layer.hs, layer.sh_off
+        s1, s3, s2 = layer._shared_w()
+        run("shared_up", lambda: xm.xmoe_expert_ffn_up(x, s1, s3, so, layer.sh_act, layer.sh_h13),
+            flop=4.0 * T * d * hs)
+        run("shared_down", lambda: xm.xmoe_expert_ffn_down(layer.sh_act, s2, so, layer.sh_y), flop=2.0 * T * d * hs)
+    if wl.backward:
+        run("combine_bwd", lambda: xm.xmoe_combine_bwd(dy, layer.ye, pft, layer.dye, layer.dtopk_w_all),
+            nbytes=T * d * s + 2.0 * R * d * s + 12.0 * R)
+        run("dact", lambda: xm.xmoe_expert_ffn_bwd_dact(layer.dye, layer.W2, h13, off, layer.dh13),
+            flop=2.0 * R * d * h)
+        run("dx", lambda: xm.xmoe_expert_ffn_bwd_dx(layer.dh13, layer.W1, layer.W3, off, layer.dxs),
+            flop=4.0 * R * d * h)
+        run("dw13", lambda: xm.xmoe_expert_ffn_bwd_dw13_gather(x, pft.token_ids, layer.dh13, off, layer.dW1,
+                                                               layer.dW3), flop=4.0 * R * d * h)
+        run("dw2", lambda: xm.xmoe_expert_ffn_bwd_dw2(layer.act, layer.dye, off, layer.dW2), flop=2.0 * R * d * h)
+        if layer.side_shared:
+            run("shared_dact", lambda: xm.xmoe_expert_ffn_bwd_dact(dy, s2, layer.sh_h13, so, layer.sh_dh13),
+                flop=2.0 * T * d * hs)
+            run("shared_dx", lambda: xm.xmoe_expert_ffn_bwd_dx(layer.sh_dh13, s1, s3, so, layer.sh_dx),
+                flop=4.0 * T * d * hs)
+            run("shared_dw13", lambda: xm.xmoe_expert_ffn_bwd_dw13(x, layer.sh_dh13, so, layer._ds1, layer._ds3),
+                flop=4.0 * T * d * hs)
+            run("shared_dw2", lambda: xm.xmoe_expert_ffn_bwd_dw2(layer.sh_act, dy, so, layer._ds2),
+                flop=2.0 * T * d * hs)
+        rdx = layer.rdx
+        run("route_bwd", lambda: xm.xmoe_route_bwd(x, w["wg"], layer.logits, layer.topk_ids, layer.dtopk_w, rdx,
+                                                   layer.dwg, layer.rbwd_ws, layer.inv_tau, accumulate=False),
+            flop=4.0 * T * d * E, nbytes=4.0 * T * E + 8.0 * R + 2.0 * T * d * s + 4.0 * d * E)
+        run("dispatch_bwd", lambda: xm.xmoe_dispatch_bwd(layer.dxs, pft, T, layer.dx, dx_add=rdx),
+            nbytes=R * d * s + 2.0 * T * d * s + 4.0 * R)
+    return rows
 
 
 def pctl(v):
@@ -353,15 +441,82 @@ def ep_rbd(xm, wl, layer, stream, nodes=8, ranks=8, n_rep=20):
     rows = torch.randn(n, d, device="cuda").to(torch.bfloat16)
     dst = torch.empty_like(rows)
     t_reg = timed(lambda: xm.xmoe_scatter_rows(rows, r2l, dst))
+    # the same regroup with the 256 MB Infinity Cache flushed before each call
+    # (its ~100 MB working set otherwise stays cache-resident between calls)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    t_fl = 0.0
+    for _ in range(n_rep):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        xm.xmoe_scatter_rows(rows, r2l, dst)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_fl += e0.elapsed_time(e1) * 1e3 / n_rep
+    del flush
     moved = 2.0 * n * d * 2 + 4.0 * n  # rows read and written once, plus the index
     return {"pilots": {"nodes": nodes, "experts_per_node": E // nodes, "us": round(t_pil, 2),
                        "pilots": n_pilots, "slots": T * k, "pilot_fraction": round(n_pilots / (T * k), 4)},
             "send_plan": {"ranks": ranks, "us": round(t_send, 2)},
             "recv_plan": {"ranks": ranks, "rows": n, "us": round(t_recv, 2)},
-            "regroup": {"rows": n, "d": d, "us": round(t_reg, 2), "GB_per_s": round(moved / (t_reg * 1e-6) / 1e9, 1)}}
+            "regroup": {"rows": n, "d": d, "us_cache_resident": round(t_reg, 2),
+                        "GB_per_s_cache_resident": round(moved / (t_reg * 1e-6) / 1e9, 1),
+                        "us_cache_flushed": round(t_fl, 2),
+                        "GB_per_s_cache_flushed": round(moved / (t_fl * 1e-6) / 1e9, 1)}}
 
 
-def cpu_baseline(wl, inp, sample_tokens, layer):
+def cpu_info():
+    """CPU model, sockets and the threads this process may use (lscpu, else
+    /proc/cpuinfo)."""
+    info = {"model": None, "sockets": None, "threads_available": len(os.sched_getaffinity(0))}
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            key, _, val = line.partition(":")
+            if key.strip() == "Model name":
+                info["model"] = val.strip()
+            elif key.strip() == "Socket(s)":
+                info["sockets"] = int(val.strip()) if val.strip().isdigit() else val.strip()
+    except (OSError, ValueError):
+        pass
+    if info["model"] is None:
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for line in fh:
+                    if line.startswith("model name"):
+                        info["model"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    return info
+
+
+def oracle_tiny_single_thread(reps=3):
+    """The oracle's forward of the tiny fp32 workload (256 tokens, d 128, 8
+    experts of 64, top-2) on one thread, median of `reps` runs."""
+    import numpy as np
+
+    import oracle as orc
+    import workloads
+
+    wl = workloads.get("tiny_f32")
+    inp = workloads.generate(wl, backward=False)
+    o = {k: v.numpy() for k, v in inp.items() if v is not None}
+    prev = orc.get_threads()
+    orc.set_threads(1)
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        orc.layer_forward(o, wl.k, 0, wl.inv_tau)
+        ts.append(time.perf_counter() - t0)
+    orc.set_threads(prev)
+    t = float(np.median(ts))
+    return {"workload": "tiny_f32 forward", "threads": 1, "seconds_median": round(t, 5), "runs": reps,
+            "gflops": round(wl.useful_flops()["fwd"] / t / 1e9, 3), "tokens_per_s": round(wl.T / t, 1)}
+
+
+def cpu_baseline(wl, inp, sample_tokens, layer, full_runs=0):
     """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
     same inputs: full forward and backward (routing, experts, shared experts,
     combine, all gradients) for those tokens; throughput scaled per token.
@@ -395,7 +550,26 @@ def cpu_baseline(wl, inp, sample_tokens, layer):
     what = "full forward+backward incl. all weight gradients" if wl.backward else "full forward"
     base = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOPS", "cores": orc.get_threads(), "kind": "oracle",
             "sample": f"{n} of {wl.T} tokens, {what}",
-            "seconds": round(dt, 2), "tokens_per_s": round(n / dt, 2)}
+            "seconds": round(dt, 2), "tokens_per_s": round(n / dt, 2), "cpu": cpu_info(),
+            "single_thread_tiny": oracle_tiny_single_thread()}
+    if full_runs > 0:
+        # the whole workload, as many runs as asked (median)
+        import numpy as np
+        full = {k: v for k, v in o.items()}
+        full["x"] = bits(inp["x"])
+        full["dy"] = bits(inp["dy"])
+        ts = []
+        for _ in range(full_runs):
+            t1 = time.perf_counter()
+            f2 = orc.layer_forward(full, wl.k, 1, wl.inv_tau, n_shared=wl.n_shared)
+            if wl.backward:
+                orc.layer_backward(full, f2, full["dy"], wl.inv_tau, n_shared=wl.n_shared)
+            ts.append(time.perf_counter() - t1)
+            print(f"oracle full run {len(ts)}/{full_runs}: {ts[-1]:.1f} s", file=sys.stderr, flush=True)
+        tm = float(np.median(ts))
+        base["full_workload"] = {"tokens": wl.T, "runs": full_runs, "seconds_median": round(tm, 2),
+                                 "tflops": round(wl.useful_flops()["total"] / tm / 1e12, 6),
+                                 "tokens_per_s": round(wl.T / tm, 2)}
     ok = (layer.topk_ids[:n].cpu().numpy() == fwd["route"]["topk_ids"]).all(axis=1)
 
     def rel(g, r):

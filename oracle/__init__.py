@@ -21,7 +21,9 @@ from typing import Dict, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# XMOE_ORACLE_LIB names another build of oracle.c: the mutation check of the
+# pins (tests/test_oracle_mutants.py) loads copies with planted mistakes this way
+_LIB_PATH = os.environ.get("XMOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2

@@ -12,12 +12,17 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(HERE, "oracle.c")
-    out = os.path.join(HERE, "liboracle.so")
+FLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+         "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(verbose: bool = False, src: str = None, out: str = None, extra=()) -> str:
+    """Compile oracle.c (or `src`, e.g. a copy with a planted mistake for the
+    pins' mutation check) into liboracle.so (or `out`)."""
+    src = src or os.path.join(HERE, "oracle.c")
+    out = out or os.path.join(HERE, "liboracle.so")
     tmp = out + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter", src, "-o", tmp, "-lm"]
+    cmd = ["gcc"] + FLAGS + list(extra) + [src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
