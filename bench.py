@@ -294,6 +294,11 @@ def main():
     out["value_cache_flushed"] = round(flops["total"] / (out["step_ms_cache_flushed"]["median"] * 1e-3) / 1e12, 2)
     out["breakdown_ms_serial"] = {k: round(v, 4) for k, v in breakdown.items()}
     roofline["per_product"] = per_product(xm, wl, layer, weights, x, dy, stream)
+    # the products alone leave the layer's buffers with partial results (the
+    # dispatch backward without the shared experts' input gradient): one more
+    # whole step restores them before anything below reads the outputs
+    step()
+    torch.cuda.synchronize()
     out["ep_rbd"] = ep_rbd(xm, wl, layer, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(wl, inp, args.cpu_sample_tokens, layer, args.cpu_full)
@@ -303,7 +308,8 @@ def main():
 def per_product(xm, wl, layer, weights, x, dy, stream, reps=20):
     """Every product of the step alone: 3 untimed calls, then `reps` calls back
     to back between two events, on the layer's own buffers (after the timed
-    steps, so they hold one step's values).  Matrix-core products report
+    steps, so they hold one step's values; some calls overwrite outputs with
+    partial results, so the caller reruns a whole step afterwards).  Matrix-core products report
     TFLOP/s against the bf16 peak; the row kernels, the router and its
     backward report algorithmic GB/s against HBM (each input read once, each
     output written once), the PFT build microseconds."""

@@ -76,6 +76,10 @@ bool ksplit_fills(int E, int64_t m, int64_t n, int bm) {
     return static_cast<int64_t>(E) * ((m + bm - 1) / bm) * ((n + bm - 1) / bm) >= 256;
 }
 
+// The weight gradients give each XCD whole experts (runs of one expert's
+// tiles): an expert's rows and row gradients, a few MB, are then fetched into
+// one L2 instead of several.  Measured on the DeepSeek-MoE-16B shape: dW1/dW3
+// 0.413 -> 0.390 ms; dW2 level.
 GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
     GemmArgs p{};
     p.group_mode = GM_KSPLIT;
@@ -83,6 +87,7 @@ GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
     p.G = E;
     p.extent = rows;
     p.nphase = 1;
+    p.xcd_run = -1;
     return p;
 }
 

@@ -66,6 +66,10 @@ struct GemmArgs {
     // fp32 outputs with EPI_STORE: nonzero adds the products to C (C0 and Cx)
     // instead of overwriting it (one fp32 addition per element)
     int accum;
+    // tiles per XCD run of the block -> tile map: 0 = kXcdRun; -1 = the tiles
+    // of one group (GM_KSPLIT: exact; GM_ROWS: the mean group's), so that a
+    // group's operands are fetched into one XCD's L2
+    int xcd_run;
 };
 
 // ---------------------------------------------------------------- epilogues
@@ -121,9 +125,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, int64_t cbase_row, i
 
 struct Tile {
     int g;          // group
-    int mt, nt;     // tile coordinates inside the group
+    int m0, nt;     // first row of the tile inside the group; column tile
     int64_t base;   // GM_ROWS: first row of the group; GM_KSPLIT: first k of the group
-    int Mg, Kg;     // extents of the group
+    int Mg, Kg;     // row extent of the group and K extent
 };
 
 __device__ __forceinline__ void seg_bounds(const GemmArgs &p, int g, int64_t *lo, int64_t *hi) {
@@ -152,12 +156,23 @@ __device__ __forceinline__ void seg_bounds(const GemmArgs &p, int g, int64_t *lo
 constexpr int kXcds = 8;
 constexpr int kXcdRun = 32;
 
-__device__ __forceinline__ int xcd_tile_order(int b, int nblocks) {
-    constexpr int W = kXcds * kXcdRun;
+__device__ __forceinline__ int xcd_tile_order(int b, int nblocks, int run = kXcdRun) {
+    const int W = kXcds * run;
     const int full = nblocks / W * W;
     if (b >= full) return b;
     const int xcd = b % kXcds, local = b / kXcds;
-    return (local / kXcdRun) * W + xcd * kXcdRun + local % kXcdRun;
+    return (local / run) * W + xcd * run + local % run;
+}
+
+// the run length of a launch (see GemmArgs::xcd_run)
+template <int BM, int BN>
+__device__ __forceinline__ int xcd_run_of(const GemmArgs &p) {
+    if (p.xcd_run > 0) return p.xcd_run;
+    if (p.xcd_run == 0) return kXcdRun;
+    const int tiles_n = (p.N + BN - 1) / BN;
+    if (p.group_mode == GM_KSPLIT) return ((p.M + BM - 1) / BM) * tiles_n;
+    const int64_t per = (p.extent + static_cast<int64_t>(BM) * p.G - 1) / (static_cast<int64_t>(BM) * p.G);
+    return static_cast<int>(per > 0 ? per : 1) * tiles_n;
 }
 
 // Resolve this block's tile.  Returns false when the block has no tile.
@@ -169,15 +184,16 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t, int block, int nblocks)
     if (p.group_mode == GM_KSPLIT) {
         const int tiles_m = (p.M + BM - 1) / BM;
         const int per_g = tiles_m * tiles_n;
-        const int bid = xcd_tile_order(block, nblocks);
+        const int bid = xcd_tile_order(block, nblocks, xcd_run_of<BM, BN>(p));
         const int g = bid / per_g;
         if (g >= p.G) return false;
         const int rem = bid - g * per_g;
         int64_t lo, hi;
         seg_bounds(p, g, &lo, &hi);
+        const int mt = rem / tiles_n;
         t->g = g;
-        t->mt = rem / tiles_n;
-        t->nt = rem - t->mt * tiles_n;
+        t->m0 = mt * BM;
+        t->nt = rem - mt * tiles_n;
         t->base = lo;
         t->Mg = p.M;
         t->Kg = static_cast<int>(hi - lo);
@@ -203,7 +219,7 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t, int block, int nblocks)
             if (lane >= off) inc += v;
         }
         const int exc = inc - cnt;
-        const int bid = xcd_tile_order(block, nblocks);
+        const int bid = xcd_tile_order(block, nblocks, xcd_run_of<BM, BN>(p));
         const int mt_global = bid / tiles_n;   // past the last group's tiles: no tile
         if (mt_global >= exc && mt_global < inc) {
             int b = exc;
@@ -228,12 +244,13 @@ __device__ bool resolve_tile(const GemmArgs &p, Tile *t, int block, int nblocks)
     if (g < 0) return false;
     int64_t lo, hi;
     seg_bounds(p, g, &lo, &hi);
+    const int mt = s_res[1];
     t->g = g;
-    t->mt = s_res[1];
     t->nt = s_res[2];
     t->base = lo;
-    t->Mg = static_cast<int>(hi - lo);
     t->Kg = p.K;
+    t->m0 = mt * BM;
+    t->Mg = static_cast<int>(hi - lo);
     return true;
 }
 
@@ -556,6 +573,204 @@ struct FragAddr {
     }
 };
 
+// The epilogue of a BM x BN tile held as accumulators acc[NB][TM][TN] by
+// WGM x WGN waves (the layout both pipelined kernels produce), with the
+// kernel's idle operand ring (RING bytes of LDS at smem / sbase) as staging.
+template <int BM, int BN, int WGM, int WGN, int NB, int RING, int EPI, typename OutT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, const Tile &t, const GroupPtrs<bf16_t> &q,
+                                              f32x16_t (&acc)[NB][BM / WGM / 32][BN / WGN / 32], char *smem,
+                                              uint32_t sbase, int m0, int n0, int lane, int wave) {
+    constexpr int NW = WGM * WGN, NT = 64 * NW;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    const int wm = wave / WGN, wn = wave % WGN;
+    // accumulator (i, j, r) of lane l holds C[row, col] with
+    //   row = i*32 + l%32,  col = j*32 + 8*(r/4) + 4*(l/32) + r%4
+    const int m_lane = m0 + wm * WTM + (lane & 31);
+    const int n_lane = n0 + wn * WTN + 4 * (lane >> 5);
+    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
+        // Staged epilogue: each output matrix goes through the (now idle) ring
+        // as a padded row-major bf16 tile, then leaves in 16-byte row chunks
+        // (16 lanes per 256-byte row segment) instead of 8-byte pieces.
+        constexpr int LDC = BN + 8;
+        // two passes (one per row half, i.e. per wave row) when the tile does not fit the ring
+        constexpr int kPass = BM * LDC * 2 <= RING ? 1 : WGM;  // 1 pass, or one per wave row
+        constexpr int RP = BM / kPass;  // rows per pass
+        static_assert(RP * LDC * 2 <= RING, "output tile must fit the ring");
+        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        __bf16 *cs = reinterpret_cast<__bf16 *>(smem);
+        const int nout = EPI == EPI_SWIGLU ? (p.aux_out ? 3 : 1) : ((NB == 2 && p.Cx) ? 2 : 1);
+        __syncthreads();  // every wave is done with the ring
+        for (int o = 0; o < nout; ++o) {
+            __bf16 *dst;
+            int64_t ld;
+            if constexpr (EPI == EPI_SWIGLU) {
+                dst = o == 0 ? static_cast<__bf16 *>(p.C0) + q.crow * p.ldc
+                             : static_cast<__bf16 *>(p.aux_out) + q.crow * p.ld_aux + (o == 2 ? p.hoff : 0);
+                ld = o == 0 ? p.ldc : p.ld_aux;
+            } else {
+                dst = static_cast<__bf16 *>(o == 0 ? p.C0 : p.Cx) + q.coff + q.crow * p.ldc;
+                ld = p.ldc;
+            }
+            for (int pass = 0; pass < kPass; ++pass) {
+                if (kPass == 1 || wm == pass) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                f4_t v;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float a = acc[0][i][j][4 * g + r], b = acc[NB - 1][i][j][4 * g + r];
+                                    float x;
+                                    if constexpr (EPI == EPI_SWIGLU)
+                                        x = o == 0 ? a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * b : (o == 1 ? a : b);
+                                    else
+                                        x = o == 0 ? a : b;
+                                    v[r] = x;
+                                }
+                                const int row = (kPass == 1 ? wm * WTM : 0) + i * 32 + (lane & 31);
+                                const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                                *reinterpret_cast<bf4_t *>(cs + row * LDC + col) = __builtin_convertvector(v, bf4_t);
+                            }
+                }
+                __syncthreads();
+#pragma unroll 4
+                for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
+                    const int row = c / (BN / 8), c8 = c % (BN / 8);
+                    const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
+                    if (m < t.Mg && n < p.N)
+                        *reinterpret_cast<uint4 *>(dst + m * ld + n) =
+                            *reinterpret_cast<const uint4 *>(cs + row * LDC + 8 * c8);
+                }
+                if (o + 1 < nout || pass + 1 < kPass) __syncthreads();
+            }
+        }
+        return;
+    }
+    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_SWIGLU_BWD || EPI == EPI_ACCUM)) {
+        // Staged read-modify-write epilogue, one pass of rows at a time: the
+        // tiles the epilogue reads (SwiGLU backward: the saved H1 and H3;
+        // accumulate: C itself) come into the (now idle) ring by LDS DMA with
+        // every load of the pass in flight at once, each lane combines its
+        // accumulators with the values at the same places in place (dA, H1, H3
+        // -> dH1, dH3; or C + acc), and the tiles leave in 16-byte row chunks.
+        // Rows are unpadded; 16-byte chunk c of tile row r sits at chunk
+        // c ^ (r % 16), which keeps the lanes' 8-byte reads (32 rows, one
+        // column) and the row reads free of bank conflicts.
+        constexpr int NA = EPI == EPI_SWIGLU_BWD ? 2 : 1;  // tiles read and written
+        constexpr int kRowB = BN * 2;
+        constexpr int kCpr = BN / 8;
+        static_assert(kCpr >= 16 && (kCpr & (kCpr - 1)) == 0, "the chunk swizzle needs 16, 32, ... chunks a row");
+        // wave rows per pass: all of them if the tiles fit the ring, else half, else one
+        constexpr int WPP = NA * BM * kRowB <= RING                         ? WGM
+                            : (WGM % 2 == 0 && NA * BM / 2 * kRowB <= RING) ? WGM / 2
+                                                                                  : 1;
+        constexpr int kPass = WGM / WPP, RP = WPP * WTM;
+        static_assert(NA * RP * kRowB <= RING, "the tiles of a pass must fit the ring");
+        constexpr int kBlk = RP * kRowB / 1024;  // 1 KiB loads per tile and pass
+        static_assert(kBlk % NW == 0, "whole loads per wave");
+        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        char *const t1 = smem, *const t3 = smem + RP * kRowB;
+        // the rows read back (this tile's; rows past the group's end read as zeros)
+        const bf16_t *const rsrc_base = EPI == EPI_SWIGLU_BWD ? static_cast<const bf16_t *>(p.aux)
+                                                              : static_cast<const bf16_t *>(p.C0);
+        const int64_t ld_in = EPI == EPI_SWIGLU_BWD ? p.ld_aux : p.ldc;
+        const __amdgpu_buffer_rsrc_t raux =
+            make_rsrc(rsrc_base + (EPI == EPI_ACCUM ? q.coff : 0) + (q.crow + m0) * ld_in,
+                      static_cast<int64_t>(t.Mg - m0) * ld_in * 2);
+        __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.coff + q.crow * p.ldc;
+        __syncthreads();  // every wave is done with the ring
+        for (int pass = 0; pass < kPass; ++pass) {
+#pragma unroll
+            for (int x = 0; x < kBlk / NW; ++x) {
+                const int blk = x * NW + wave;
+                const int o = blk * 1024 + lane * 16;
+                const int row = o / kRowB, c = ((o % kRowB) / 16) ^ (row & 15);
+                const int col = n0 + 8 * c;
+                const int off = static_cast<int>(((pass * RP + row) * ld_in + col) * 2);
+                const bool ok = col < p.N;
+                lds_dma16(raux, ok ? off : kOob, sbase + blk * 1024);
+                if constexpr (NA == 2)
+                    lds_dma16(raux, ok ? off + static_cast<int>(p.hoff * 2) : kOob, sbase + RP * kRowB + blk * 1024);
+            }
+            wait_vmem<0>();
+            __syncthreads();
+            if (wm / WPP == pass) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int row = (wm % WPP) * WTM + i * 32 + (lane & 31);
+                            const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                            const int at = row * kRowB + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7);
+                            bf4_t *p1 = reinterpret_cast<bf4_t *>(t1 + at);
+                            const f4_t h1 = __builtin_convertvector(*p1, f4_t);
+                            if constexpr (NA == 2) {
+                                bf4_t *p3 = reinterpret_cast<bf4_t *>(t3 + at);
+                                const f4_t h3 = __builtin_convertvector(*p3, f4_t);
+                                f4_t g1, g3;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) {
+                                    const float v0 = acc[0][i][j][4 * g + r];
+                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
+                                    g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
+                                    g3[r] = v0 * h1[r] * sg;
+                                }
+                                *p1 = __builtin_convertvector(g1, bf4_t);
+                                *p3 = __builtin_convertvector(g3, bf4_t);
+                            } else {
+                                f4_t c1;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) c1[r] = h1[r] + acc[0][i][j][4 * g + r];
+                                *p1 = __builtin_convertvector(c1, bf4_t);
+                            }
+                        }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int c = threadIdx.x; c < RP * kCpr; c += NT) {
+                const int row = c / kCpr, c8 = c % kCpr;
+                const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
+                if (m < t.Mg && n < p.N) {
+                    const int at = row * kRowB + 16 * (c8 ^ (row & 15));
+                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) = *reinterpret_cast<const uint4 *>(t1 + at);
+                    if constexpr (NA == 2)
+                        *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
+                            *reinterpret_cast<const uint4 *>(t3 + at);
+                }
+            }
+            if (pass + 1 < kPass) __syncthreads();
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m_lane + i * 32;
+        if (m >= t.Mg) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n_lane + j * 32 + 8 * g;
+                if (n >= p.N) continue;
+                float v0[4], v1[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v0[r] = acc[0][i][j][4 * g + r];
+                    v1[r] = acc[NB - 1][i][j][4 * g + r];
+                }
+                epilogue4<EPI, OutT>(p, q.crow, q.coff, m, n, v0, v1);
+            }
+    }
+}
+
 // BM x (NB*BN) output tile per block of WGM x WGN waves, BK-deep k blocks on
 // an S-slot LDS ring.  Per k step (16 of k) each wave issues its NB*TN*TM
 // matrix-core products interleaved with the fragment reads of the next step
@@ -619,7 +834,7 @@ void gemm_dma_kernel(GemmArgs p) {
         t.Kg = min(t.Kg, kstart + p.kpart_len);
         q.coff += static_cast<int64_t>(kpart) * p.c_gstride;
     }
-    const int m0 = t.mt * BM, n0 = t.nt * BN;
+    const int m0 = t.m0, n0 = t.nt * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
@@ -850,192 +1065,7 @@ void gemm_dma_kernel(GemmArgs p) {
     if (wact) k_loop(std::true_type{});
     else k_loop(std::false_type{});
     wait_vmem<0>();  // no load may still target LDS when the block ends
-
-    // accumulator (i, j, r) of lane l holds C[row, col] with
-    //   row = i*32 + l%32,  col = j*32 + 8*(r/4) + 4*(l/32) + r%4
-    const int m_lane = m0 + wm * WTM + (lane & 31);
-    const int n_lane = n0 + wn * WTN + 4 * (lane >> 5);
-    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
-        // Staged epilogue: each output matrix goes through the (now idle) ring
-        // as a padded row-major bf16 tile, then leaves in 16-byte row chunks
-        // (16 lanes per 256-byte row segment) instead of 8-byte pieces.
-        constexpr int LDC = BN + 8;
-        // two passes (one per row half, i.e. per wave row) when the tile does not fit the ring
-        constexpr int kPass = BM * LDC * 2 <= S * kStage ? 1 : WGM;  // 1 pass, or one per wave row
-        constexpr int RP = BM / kPass;  // rows per pass
-        static_assert(RP * LDC * 2 <= S * kStage, "output tile must fit the ring");
-        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
-        typedef float f4_t __attribute__((ext_vector_type(4)));
-        __bf16 *cs = reinterpret_cast<__bf16 *>(smem);
-        const int nout = EPI == EPI_SWIGLU ? (p.aux_out ? 3 : 1) : ((NB == 2 && p.Cx) ? 2 : 1);
-        __syncthreads();  // every wave is done with the ring
-        for (int o = 0; o < nout; ++o) {
-            __bf16 *dst;
-            int64_t ld;
-            if constexpr (EPI == EPI_SWIGLU) {
-                dst = o == 0 ? static_cast<__bf16 *>(p.C0) + q.crow * p.ldc
-                             : static_cast<__bf16 *>(p.aux_out) + q.crow * p.ld_aux + (o == 2 ? p.hoff : 0);
-                ld = o == 0 ? p.ldc : p.ld_aux;
-            } else {
-                dst = static_cast<__bf16 *>(o == 0 ? p.C0 : p.Cx) + q.coff + q.crow * p.ldc;
-                ld = p.ldc;
-            }
-            for (int pass = 0; pass < kPass; ++pass) {
-                if (kPass == 1 || wm == pass) {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                f4_t v;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    const float a = acc[0][i][j][4 * g + r], b = acc[NB - 1][i][j][4 * g + r];
-                                    float x;
-                                    if constexpr (EPI == EPI_SWIGLU)
-                                        x = o == 0 ? a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * b : (o == 1 ? a : b);
-                                    else
-                                        x = o == 0 ? a : b;
-                                    v[r] = x;
-                                }
-                                const int row = (kPass == 1 ? wm * WTM : 0) + i * 32 + (lane & 31);
-                                const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                                *reinterpret_cast<bf4_t *>(cs + row * LDC + col) = __builtin_convertvector(v, bf4_t);
-                            }
-                }
-                __syncthreads();
-#pragma unroll 4
-                for (int c = threadIdx.x; c < RP * BN / 8; c += NT) {
-                    const int row = c / (BN / 8), c8 = c % (BN / 8);
-                    const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
-                    if (m < t.Mg && n < p.N)
-                        *reinterpret_cast<uint4 *>(dst + m * ld + n) =
-                            *reinterpret_cast<const uint4 *>(cs + row * LDC + 8 * c8);
-                }
-                if (o + 1 < nout || pass + 1 < kPass) __syncthreads();
-            }
-        }
-        return;
-    }
-    if constexpr (std::is_same<OutT, bf16_t>::value && (EPI == EPI_SWIGLU_BWD || EPI == EPI_ACCUM)) {
-        // Staged read-modify-write epilogue, one pass of rows at a time: the
-        // tiles the epilogue reads (SwiGLU backward: the saved H1 and H3;
-        // accumulate: C itself) come into the (now idle) ring by LDS DMA with
-        // every load of the pass in flight at once, each lane combines its
-        // accumulators with the values at the same places in place (dA, H1, H3
-        // -> dH1, dH3; or C + acc), and the tiles leave in 16-byte row chunks.
-        // Rows are unpadded; 16-byte chunk c of tile row r sits at chunk
-        // c ^ (r % 16), which keeps the lanes' 8-byte reads (32 rows, one
-        // column) and the row reads free of bank conflicts.
-        constexpr int NA = EPI == EPI_SWIGLU_BWD ? 2 : 1;  // tiles read and written
-        constexpr int kRowB = BN * 2;
-        constexpr int kCpr = BN / 8;
-        static_assert(kCpr >= 16 && (kCpr & (kCpr - 1)) == 0, "the chunk swizzle needs 16, 32, ... chunks a row");
-        // wave rows per pass: all of them if the tiles fit the ring, else half, else one
-        constexpr int WPP = NA * BM * kRowB <= S * kStage                         ? WGM
-                            : (WGM % 2 == 0 && NA * BM / 2 * kRowB <= S * kStage) ? WGM / 2
-                                                                                  : 1;
-        constexpr int kPass = WGM / WPP, RP = WPP * WTM;
-        static_assert(NA * RP * kRowB <= S * kStage, "the tiles of a pass must fit the ring");
-        constexpr int kBlk = RP * kRowB / 1024;  // 1 KiB loads per tile and pass
-        static_assert(kBlk % NW == 0, "whole loads per wave");
-        typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
-        typedef float f4_t __attribute__((ext_vector_type(4)));
-        char *const t1 = smem, *const t3 = smem + RP * kRowB;
-        // the rows read back (this tile's; rows past the group's end read as zeros)
-        const bf16_t *const rsrc_base = EPI == EPI_SWIGLU_BWD ? static_cast<const bf16_t *>(p.aux)
-                                                              : static_cast<const bf16_t *>(p.C0);
-        const int64_t ld_in = EPI == EPI_SWIGLU_BWD ? p.ld_aux : p.ldc;
-        const __amdgpu_buffer_rsrc_t raux =
-            make_rsrc(rsrc_base + (EPI == EPI_ACCUM ? q.coff : 0) + (q.crow + m0) * ld_in,
-                      static_cast<int64_t>(t.Mg - m0) * ld_in * 2);
-        __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.coff + q.crow * p.ldc;
-        __syncthreads();  // every wave is done with the ring
-        for (int pass = 0; pass < kPass; ++pass) {
-#pragma unroll
-            for (int x = 0; x < kBlk / NW; ++x) {
-                const int blk = x * NW + wave;
-                const int o = blk * 1024 + lane * 16;
-                const int row = o / kRowB, c = ((o % kRowB) / 16) ^ (row & 15);
-                const int col = n0 + 8 * c;
-                const int off = static_cast<int>(((pass * RP + row) * ld_in + col) * 2);
-                const bool ok = col < p.N;
-                lds_dma16(raux, ok ? off : kOob, sbase + blk * 1024);
-                if constexpr (NA == 2)
-                    lds_dma16(raux, ok ? off + static_cast<int>(p.hoff * 2) : kOob, sbase + RP * kRowB + blk * 1024);
-            }
-            wait_vmem<0>();
-            __syncthreads();
-            if (wm / WPP == pass) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int row = (wm % WPP) * WTM + i * 32 + (lane & 31);
-                            const int col = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                            const int at = row * kRowB + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7);
-                            bf4_t *p1 = reinterpret_cast<bf4_t *>(t1 + at);
-                            const f4_t h1 = __builtin_convertvector(*p1, f4_t);
-                            if constexpr (NA == 2) {
-                                bf4_t *p3 = reinterpret_cast<bf4_t *>(t3 + at);
-                                const f4_t h3 = __builtin_convertvector(*p3, f4_t);
-                                f4_t g1, g3;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    const float v0 = acc[0][i][j][4 * g + r];
-                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
-                                    g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
-                                    g3[r] = v0 * h1[r] * sg;
-                                }
-                                *p1 = __builtin_convertvector(g1, bf4_t);
-                                *p3 = __builtin_convertvector(g3, bf4_t);
-                            } else {
-                                f4_t c1;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) c1[r] = h1[r] + acc[0][i][j][4 * g + r];
-                                *p1 = __builtin_convertvector(c1, bf4_t);
-                            }
-                        }
-            }
-            __syncthreads();
-#pragma unroll 4
-            for (int c = threadIdx.x; c < RP * kCpr; c += NT) {
-                const int row = c / kCpr, c8 = c % kCpr;
-                const int m = m0 + pass * RP + row, n = n0 + 8 * c8;
-                if (m < t.Mg && n < p.N) {
-                    const int at = row * kRowB + 16 * (c8 ^ (row & 15));
-                    *reinterpret_cast<uint4 *>(dst + m * p.ldc + n) = *reinterpret_cast<const uint4 *>(t1 + at);
-                    if constexpr (NA == 2)
-                        *reinterpret_cast<uint4 *>(dst + m * p.ldc + p.hoff + n) =
-                            *reinterpret_cast<const uint4 *>(t3 + at);
-                }
-            }
-            if (pass + 1 < kPass) __syncthreads();
-        }
-        return;
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m_lane + i * 32;
-        if (m >= t.Mg) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n_lane + j * 32 + 8 * g;
-                if (n >= p.N) continue;
-                float v0[4], v1[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v0[r] = acc[0][i][j][4 * g + r];
-                    v1[r] = acc[NB - 1][i][j][4 * g + r];
-                }
-                epilogue4<EPI, OutT>(p, q.crow, q.coff, m, n, v0, v1);
-            }
-    }
+    gemm_epilogue<BM, BN, WGM, WGN, NB, S * kStage, EPI, OutT>(p, t, q, acc, smem, sbase, m0, n0, lane, wave);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NB, bool A_KC, bool B_KC, int S, int EPI, typename OutT,
@@ -1063,7 +1093,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     Tile t;
     if (!resolve_tile<BM, BN>(p, &t, blockIdx.x, gridDim.x)) return;
     const GroupPtrs<float> q = group_ptrs<float>(p, t);
-    const int m0 = t.mt * BM, n0 = t.nt * BN;
+    const int m0 = t.m0, n0 = t.nt * BN;
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
     float acc[NB][4][4];
 #pragma unroll
