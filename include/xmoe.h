@@ -114,11 +114,14 @@ xmoe_status xmoe_query_device(int ordinal, int *is_gfx950);
  * it is the softmax input the backward needs.  With XMOE_F32 each logit is one
  * fused multiply-add per feature in ascending order; with XMOE_BF16 the sum
  * runs on bf16 matrix cores with fp32 accumulation.
- * With XMOE_BF16 the reduction over d is split into a few ranges whose fp32
- * partial sums go to `workspace` (caller-owned device memory of at least
- * xmoe_route_workspace_size bytes, 16-byte aligned, no initialisation needed,
- * dead after the call) and are added in range order, so the result is
- * deterministic; XMOE_F32 needs no workspace (it may be NULL).
+ * With XMOE_BF16 and E <= 64 one kernel forms each block of tokens' logits over
+ * the whole of d (a few fixed ranges of d, added in a fixed order) and selects
+ * in place; it needs no workspace.  With XMOE_BF16 and E > 64 the reduction over
+ * d is split into a few ranges whose fp32 partial sums go to `workspace`
+ * (caller-owned device memory of at least xmoe_route_workspace_size bytes,
+ * 16-byte aligned, no initialisation needed, dead after the call) and are added
+ * in range order.  Both are deterministic.  XMOE_F32 needs no workspace.  Where
+ * xmoe_route_workspace_size is 0, workspace may be NULL.
  * Limits: 1 <= k <= E <= 1024, d >= 1; bf16 needs d % 8 == 0 and E % 8 == 0.
  */
 xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t T, int32_t d,

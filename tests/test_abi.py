@@ -42,7 +42,11 @@ def test_workspace_queries(xm):
     assert xm.xmoe_build_pft_workspace_size(10, 8, 9) == 0          # k > E
     assert xm.xmoe_build_pft_workspace_size(10, 2000, 2) == 0       # E > 1024
     assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 64, torch.bfloat16) >= 4096 * 64 * 2
-    assert xm.xmoe_route_workspace_size(4096, 2048, 64, torch.bfloat16) >= 4096 * 64 * 4
+    # bf16 routing: up to 64 experts one fused launch (no workspace), beyond
+    # that fp32 partial sums over a split of d
+    assert xm.xmoe_route_workspace_size(4096, 2048, 64, torch.bfloat16) == 0
+    assert xm.xmoe_route_workspace_size(4096, 2048, 128, torch.bfloat16) >= 4096 * 128 * 4
+    assert xm.xmoe_route_workspace_size(4096, 2048, 160, torch.bfloat16) >= 4096 * 160 * 4
     assert xm.xmoe_route_workspace_size(4096, 2048, 64, torch.float32) == 0
     assert xm.xmoe_route_bwd_workspace_size(4096, 2048, 0, torch.bfloat16) == 0
 
@@ -59,8 +63,8 @@ def test_invalid_arguments_rejected_on_host(xm):
     assert xm._lib_route(p, p, 7, 10, 8, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 2
     # bf16 with d not a multiple of 8
     assert xm._lib_route(p, p, 1, 10, 12, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 2
-    # bf16 routing without its workspace
-    assert xm._lib_route(p, p, 1, 10, 64, 8, 2, 1.0, None, None, p, p, p, None, 0, None) == 3
+    # bf16 routing over more than 64 experts without its workspace
+    assert xm._lib_route(p, p, 1, 10, 64, 256, 2, 1.0, None, None, p, p, p, None, 0, None) == 3
     # expert FFN: h not a multiple of 8, E out of range, NULL offsets
     assert xm._lib_up(p, p, p, 1, p, 4, 100, 64, 12, p, None, None) == 2
     assert xm._lib_up(p, p, p, 1, p, 0, 100, 64, 64, p, None, None) == 1

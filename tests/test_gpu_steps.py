@@ -55,11 +55,16 @@ def test_router_fp32_is_bit_exact(xm):
     assert_close(host(w), r["topk_w"], 1e-5, "topk_w")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_router_exact_grid_ties(xm, dtype):
+@pytest.mark.parametrize("dtype,T,d,E,k", [("f32", 300, 64, 16, 4), ("bf16", 300, 64, 16, 4),
+                                          ("bf16", 77, 264, 64, 8), ("bf16", 33, 2048, 56, 6),
+                                          ("bf16", 129, 1032, 200, 8)])
+def test_router_exact_grid_ties(xm, dtype, T, d, E, k):
     """Inputs on a coarse binary grid: every logit is exact in any summation
-    order, so the matrix-core path must match bit for bit, ties included."""
-    T, d, E, k = 300, 64, 16, 4
+    order, so the matrix-core path must match bit for bit, ties included.  The
+    bf16 shapes cover the fused kernel (up to 64 experts: a partial last
+    token block, d ending 8 past a 32-deep k block, more waves than k blocks,
+    fewer experts than its 64-wide column block) and the split-d path (200
+    experts)."""
     x, wg = workloads.exact_router_inputs(T, d, E, seed=5)
     x, wg = x.to(DT[dtype]), wg.to(DT[dtype])
     sb = torch.zeros(E)
@@ -96,12 +101,19 @@ def test_router_bf16_small(xm, name):
 @pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 384, 16), ("bf16", 130, 128, 1024, 8),
                                           ("f32", 257, 64, 10, 3), ("f32", 100, 32, 300, 5),
                                           ("f32", 64, 16, 1021, 4), ("f32", 33, 8, 1, 1),
-                                          ("bf16", 1, 2048, 160, 8), ("bf16", 7, 7168, 256, 8)])
+                                          ("bf16", 1, 2048, 160, 8), ("bf16", 7, 7168, 256, 8),
+                                          ("bf16", 1, 2048, 64, 6), ("bf16", 33, 264, 8, 2),
+                                          ("bf16", 4097, 2048, 64, 6), ("bf16", 257, 7168, 128, 8),
+                                          ("bf16", 100, 512, 72, 8), ("bf16", 65, 136, 120, 4),
+                                          ("bf16", 300, 7168, 48, 6)])
 def test_router_expert_counts(xm, dtype, T, d, E, k):
     """Expert counts beyond the workloads': more than 256 experts (16 and 32
     lanes per token in the top-k), fp32 counts that are not a multiple of 4
     (element loads instead of 16-byte vectors), a single expert; and a few
-    tokens, where the logits' d reduction is split into the most parts.  fp32 logits are
+    tokens, where the logits' d reduction is split into the most parts.  bf16
+    with up to 64 experts runs the fused kernel: expert counts below its
+    64-wide column block, one token, ragged token blocks, a d tail of 8, d =
+    7168; 72-128 experts the split-d path.  fp32 logits are
     bit-exact, so its selections must match outright; bf16 through routing_check."""
     x = workloads.random_rows(T, d, dtype, seed=E)
     wg = workloads.random_rows(d, E, dtype, seed=E + 1, std=d ** -0.5)
