@@ -76,10 +76,13 @@ bool ksplit_fills(int E, int64_t m, int64_t n, int bm) {
     return static_cast<int64_t>(E) * ((m + bm - 1) / bm) * ((n + bm - 1) / bm) >= 256;
 }
 
-// The weight gradients give each XCD whole experts (runs of one expert's
-// tiles): an expert's rows and row gradients, a few MB, are then fetched into
-// one L2 instead of several.  Measured on the DeepSeek-MoE-16B shape: dW1/dW3
-// 0.413 -> 0.390 ms; dW2 level.
+// The weight gradients give each XCD runs of half an expert's tiles: an
+// expert's rows and row gradients, a few MB, are then fetched into two L2s
+// instead of several.  Step time (dW1/dW3 alone) against runs of 32 tiles and
+// runs of a whole expert: DeepSeek-MoE-16B 2.374 (0.406) ms against 2.374
+// (0.419) and 2.369 (0.401); Zipf-skewed 5.27 against 5.33 and 5.47 ms, where
+// whole-expert runs put all the tiles of the heaviest expert (16384 rows) on
+// one XCD.
 GemmArgs ksplit_args(const int32_t *offsets, int E, int64_t rows) {
     GemmArgs p{};
     p.group_mode = GM_KSPLIT;

@@ -66,9 +66,9 @@ struct GemmArgs {
     // fp32 outputs with EPI_STORE: nonzero adds the products to C (C0 and Cx)
     // instead of overwriting it (one fp32 addition per element)
     int accum;
-    // tiles per XCD run of the block -> tile map: 0 = kXcdRun; -1 = the tiles
-    // of one group (GM_KSPLIT: exact; GM_ROWS: the mean group's), so that a
-    // group's operands are fetched into one XCD's L2
+    // tiles per XCD run of the block -> tile map: 0 = kXcdRun; -1 = GM_KSPLIT:
+    // half of one group's tiles, so that two XCDs share a group's operands
+    // (GM_ROWS: the mean group's tiles)
     int xcd_run;
 };
 
@@ -170,7 +170,7 @@ __device__ __forceinline__ int xcd_run_of(const GemmArgs &p) {
     if (p.xcd_run > 0) return p.xcd_run;
     if (p.xcd_run == 0) return kXcdRun;
     const int tiles_n = (p.N + BN - 1) / BN;
-    if (p.group_mode == GM_KSPLIT) return ((p.M + BM - 1) / BM) * tiles_n;
+    if (p.group_mode == GM_KSPLIT) return (((p.M + BM - 1) / BM) * tiles_n + 1) / 2;
     const int64_t per = (p.extent + static_cast<int64_t>(BM) * p.G - 1) / (static_cast<int64_t>(BM) * p.G);
     return static_cast<int>(per > 0 ? per : 1) * tiles_n;
 }
