@@ -105,7 +105,8 @@ def test_router_bf16_small(xm, name):
                                           ("bf16", 1, 2048, 64, 6), ("bf16", 33, 264, 8, 2),
                                           ("bf16", 4097, 2048, 64, 6), ("bf16", 257, 7168, 128, 8),
                                           ("bf16", 100, 512, 72, 8), ("bf16", 65, 136, 120, 4),
-                                          ("bf16", 300, 7168, 48, 6)])
+                                          ("bf16", 300, 7168, 48, 6), ("bf16", 50, 8, 16, 4),
+                                          ("bf16", 40, 24, 64, 64)])
 def test_router_expert_counts(xm, dtype, T, d, E, k):
     """Expert counts beyond the workloads': more than 256 experts (16 and 32
     lanes per token in the top-k), fp32 counts that are not a multiple of 4
@@ -113,7 +114,8 @@ def test_router_expert_counts(xm, dtype, T, d, E, k):
     tokens, where the logits' d reduction is split into the most parts.  bf16
     with up to 64 experts runs the fused kernel: expert counts below its
     64-wide column block, one token, ragged token blocks, a d tail of 8, d =
-    7168; 72-128 experts the split-d path.  fp32 logits are
+    7168, d = 8 (one k block, seven idle waves), k = E = 64; 72-128 experts
+    the split-d path.  fp32 logits are
     bit-exact, so its selections must match outright; bf16 through routing_check."""
     x = workloads.random_rows(T, d, dtype, seed=E)
     wg = workloads.random_rows(d, E, dtype, seed=E + 1, std=d ** -0.5)
