@@ -58,6 +58,33 @@ def test_layer_forward_backward(xm, name, merge, lean):
     routed buffer instead of as their own FFN on a second stream."""
     wl = workloads.small(name)
     inp = workloads.generate(wl, backward=True)
+    tag = f"layer {name}" + ("-merged" if merge else "") + ("-lean" if lean else "")
+    check_layer(xm, wl, inp, tag, lean=lean, merge=merge)
+
+
+# Degenerate layers: one token (64 experts, 58 of them empty, through the
+# fused router), top-1, every token to every expert, a single fp32 expert, and
+# widths that are no tile multiple.
+DEGENERATE = [
+    workloads.Workload("one_token", "bf16", T=1, d=256, E=64, h=96, k=6, backward=True),
+    workloads.Workload("top1", "bf16", T=37, d=128, E=8, h=64, k=1, backward=True),
+    workloads.Workload("k_equals_E", "bf16", T=96, d=128, E=8, h=64, k=8, backward=True),
+    workloads.Workload("one_expert_f32", "f32", T=50, d=64, E=1, h=32, k=1, backward=True),
+    workloads.Workload("ragged_widths", "bf16", T=70, d=72, E=16, h=40, k=3, n_shared=1, h_shared=24,
+                       backward=True),
+]
+
+
+@pytest.mark.parametrize("wl", DEGENERATE, ids=[w.name for w in DEGENERATE])
+def test_layer_degenerate(xm, wl):
+    inp = workloads.generate(wl, backward=True)
+    check_layer(xm, wl, inp, f"layer {wl.name}")
+
+
+def check_layer(xm, wl, inp, tag, lean=False, merge=False):
+    """The GPU layer against the oracle's layer on the same inputs: routing,
+    the PFT, y, dX, the routing weights' gradient, the shared and routed weight
+    gradients and dWg."""
     layer = run_layer(xm, wl, inp, lean=lean, merge=merge)
     assert layer.merged == (merge and wl.n_shared > 0)
     o = _oracle_inputs(inp)
@@ -71,7 +98,6 @@ def test_layer_forward_backward(xm, name, merge, lean):
     gids = host(layer.topk_ids)
     stats = {}
     mism = routing_check(gids, host(layer.logits), fwd["route"], sb, wl.k, 1e-5, stats=stats)
-    tag = f"layer {name}" + ("-merged" if merge else "") + ("-lean" if lean else "")
     near_tie_bound(tag, stats, wl.T)
     if wl.dtype == "f32":
         np.testing.assert_array_equal(host(layer.logits), fwd["route"]["scores"])
