@@ -169,13 +169,13 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
     p.aux = h13;
     p.ld_aux = 2 * static_cast<int64_t>(h);
     p.hoff = h;
-    // the 256-row tile from 1024 rows per expert only: below that it is faster
-    // alone when the last tiles are well filled (384 rows: 232 against 255 us),
-    // but in the layer's step, beside the shared experts' and the weight
-    // gradients' products, the 128-row tile (two blocks per compute unit) made
-    // the whole DeepSeek-MoE-16B step 0.7% faster (three alternations)
+    // the 256-row tile on the down-projection's rule (an expert's last 256-row
+    // tile well filled): at 384 rows per expert routed dA 0.262 -> 0.242 ms
+    // alone, the DeepSeek-MoE-16B step level (with dW1/dW3 beside dA and dX on
+    // the caller's stream; with dW1/dW3 on the weight-gradient stream the
+    // 128-row tile had made the step 0.7% faster)
     err = dt != kBF16 ? launch_gemm_f32<1, true, true, EPI_SWIGLU_BWD>(p, s)
-          : large_tiles(rows, E, h, 256)
+          : large_tiles_filled(rows, E, h, 256)
               ? launch_gemm_dma<256, 256, 32, 4, 2, 1, true, true, 4, EPI_SWIGLU_BWD, bf16_t, 1>(p, s)
                                          : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, true, 3, EPI_SWIGLU_BWD, bf16_t, 2>(p, s);
     return err;
