@@ -112,8 +112,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
-              f"across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer is not sharded "
+              f"across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 
