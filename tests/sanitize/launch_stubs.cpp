@@ -1,7 +1,7 @@
 // No-op launchers with the signatures of kernels.hpp, so that api.cpp's host
 // code (argument validation, error reporting, dispatch on dtype) can be built
 // and run under the host sanitizers without any device code.  Workspace sizes
-// are fixed small values: the driver only checks the validation paths.
+// are fixed small values: api_driver.cpp only exercises the validation paths.
 #include <hip/hip_runtime.h>
 
 #include "../../padding_free_expert_amd/csrc/kernels.hpp"
