@@ -490,7 +490,6 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
         p.kpart_len = ((d / kparts + 31) / 32) * 32;
         p.c_gstride = T * E;
         switch (col_tile(E)) {
-            case 64: err = launch_gemm_dma<128, 64, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s); break;
             case 128: err = launch_gemm_dma<128, 128, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s); break;
             // E <= 192: four waves side by side over the 256 columns, so the
             // wave whose 64 columns all lie past E skips its products
