@@ -144,3 +144,49 @@ def test_y_add_is_added(orc):
     ya = _rand((T, d), 13)
     y = orc.combine(np.zeros((0, d)), np.zeros(0, np.int32), np.zeros(0), T, y_add=ya)
     np.testing.assert_array_equal(y, ya.astype(np.float64))
+
+
+def _tiny_layer_inputs():
+    wl = workloads.get("tiny_f32")
+    inp = workloads.generate(wl, backward=True)
+    return wl, {k: v.numpy() for k, v in inp.items() if v is not None}
+
+
+def test_layer_select_own_choice_changes_nothing(orc):
+    """select= hands a token's selection to the oracle's layer (the GPU tests
+    use it where a near-tie admits more than one correct selection).  Handing
+    back the oracle's own selection must change nothing, bit for bit."""
+    wl, o = _tiny_layer_inputs()
+    ref = orc.layer_forward(o, wl.k, 0)
+    own = {t: ref["route"]["topk_ids"][t].copy() for t in (0, 7, wl.T - 1)}
+    got = orc.layer_forward(o, wl.k, 0, select=own)
+    for key in ("y", "ye", "row_w"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(got["route"]["topk_ids"], ref["route"]["topk_ids"])
+
+
+def test_layer_select_other_choice_is_the_textbook_mixture(orc):
+    """Another selection for one token: every other token's output is bitwise
+    unchanged, and the token's output is sum_j p[t, e_j] * SwiGLU_{e_j}(x_t)
+    with the oracle's softmax probabilities, computed here with numpy."""
+    wl, o = _tiny_layer_inputs()
+    ref = orc.layer_forward(o, wl.k, 0)
+    t0 = 5
+    own = ref["route"]["topk_ids"][t0]
+    other = np.array([e for e in range(wl.E) if e not in own.tolist()][:wl.k], np.int32)
+    got = orc.layer_forward(o, wl.k, 0, select={t0: other})
+    keep = np.arange(wl.T) != t0
+    np.testing.assert_array_equal(got["y"][keep], ref["y"][keep])
+    p = ref["route"]["probs"][t0]
+    x = o["x"][t0:t0 + 1].astype(np.float64)
+    want = sum(p[e] * _swiglu_numpy(x, o["w1"][e].astype(np.float64), o["w3"][e].astype(np.float64),
+                                    o["w2"][e].astype(np.float64))[0] for e in other)
+    np.testing.assert_allclose(got["y"][t0], want, rtol=1e-9, atol=1e-12)
+    np.testing.assert_array_equal(got["route"]["topk_w"][t0], p[other].astype(got["route"]["topk_w"].dtype))
+
+
+@pytest.mark.parametrize("bad", [[0, 0], [0], [0, 99], [-1, 2]])
+def test_layer_select_rejects_invalid_choices(orc, bad):
+    wl, o = _tiny_layer_inputs()
+    with pytest.raises(orc.OracleError):
+        orc.layer_forward(o, wl.k, 0, select={3: np.array(bad, np.int32)})
