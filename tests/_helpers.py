@@ -249,6 +249,59 @@ def pft_invariants(ids: np.ndarray, w: np.ndarray, E: int, pft: dict):
     np.testing.assert_array_equal(pft["combine_weights"][s2r].view(np.uint32), np.asarray(w, np.float32).view(np.uint32))
 
 
+def _f64(a) -> np.ndarray:
+    """Oracle input (bf16 bit patterns as uint16, or fp32) -> float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def dx_floor(o, fwd, bwd, dy, n_shared: int = 0) -> np.ndarray:
+    """Error scale of the layer's input gradient dX, per element.
+
+    dX[t] = sum_j dXs[row(t,j)] + sum_s dXsh_s[t] + dz[t].Wg^T.  Each expert
+    term is dXs[r] = dH1[r].W1^T + dH3[r].W3^T over the expert width, whose
+    factors dH1 and dH3 carry the rounding of H1, H3 and dA: it moves them by
+    amounts that scale with |dA*H3| and |dA*H1| (swiglu_wgrad_scales), not with
+    |dH1|, |dH3|, and the magnitude used for dA again includes the root-sum-
+    square of its own terms dYe*W2.  Where one heavily weighted expert's
+    products cancel inside dXs, neither |dX| nor its rms shows that error.  The
+    scale is therefore the root-sum-square, over every term of dX[t], of the
+    magnitudes of the products inside it (expert terms as above, shared
+    experts alike with dY in place of dYe, and the gate's dz*Wg), together with
+    the terms themselves (each is rounded before the sum).  o: the oracle's
+    inputs (routed weights in the order of fwd's row experts); dy: the
+    upstream gradient of fwd's tokens; every value is an oracle (fp64) value
+    or a generator input."""
+    dx = bwd["dx"]
+    F2 = np.zeros(dx.shape)
+
+    def add(tok, da, dye, h1, h3, w1, w3, w2, dxs):
+        # w1, w3 [d, h]; w2 [h, d]; rows of da, h1, h3 [., h] and dye, dxs [., d]
+        dam = np.abs(da) + np.sqrt(np.maximum((dye * dye) @ (w2 * w2).T, 0.0))
+        m1, m3 = dam * np.abs(h3), dam * np.abs(h1)
+        np.add.at(F2, tok, (m1 * m1) @ (w1 * w1).T + (m3 * m3) @ (w3 * w3).T + dxs * dxs)
+
+    W1, W3, W2 = _f64(o["w1"]), _f64(o["w3"]), _f64(o["w2"])
+    re_, rt = fwd["row_expert"], fwd["row_token"]
+    for e in np.unique(re_):
+        r = np.nonzero(re_ == e)[0]
+        add(rt[r], bwd["da"][r], bwd["dye"][r], fwd["h1"][r], fwd["h3"][r], W1[e], W3[e], W2[e], bwd["dxs"][r])
+    if n_shared:
+        S1, S3, S2 = _f64(o["s1"]), _f64(o["s3"]), _f64(o["s2"])
+        hs = S1.shape[1] // n_shared
+        dyf = _f64(dy)
+        tok = np.arange(dx.shape[0])
+        for s_ in range(n_shared):
+            cs = slice(s_ * hs, (s_ + 1) * hs)
+            f, b = fwd["shared"][s_], bwd["shared"][s_]
+            add(tok, b["da"], dyf, f["h1"], f["h3"], S1[:, cs], S3[:, cs], S2[cs, :], b["dxs"])
+    Wg = _f64(o["wg"])
+    F2 += (bwd["dz"] ** 2) @ (Wg * Wg).T
+    return np.sqrt(F2)
+
+
 def router_wgrad_floor(x, probs, ids, ye_slot, dy, dz, inv_tau):
     """Error scale of dWg = x^T dz when dz comes out of the layer's own chain.
 
