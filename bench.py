@@ -367,7 +367,8 @@ def per_product(xm, wl, layer, weights, x, dy, stream, reps=20):
     if wl.backward:
         run("combine_bwd", lambda: xm.xmoe_combine_bwd(dy, layer.ye, pft, layer.dye, layer.dtopk_w_all),
             nbytes=T * d * s + 2.0 * R * d * s + 12.0 * R)
-        run("dact", lambda: xm.xmoe_expert_ffn_bwd_dact(layer.dye, layer.W2, h13, off, layer.dh13),
+        run("dact", lambda: xm.xmoe_expert_ffn_bwd_dact_gather(dy, pft.token_ids, pft.combine_weights, layer.W2, h13,
+                                                             off, layer.dh13),
             flop=2.0 * R * d * h)
         run("dx", lambda: xm.xmoe_expert_ffn_bwd_dx(layer.dh13, layer.W1, layer.W3, off, layer.dxs),
             flop=4.0 * R * d * h)

@@ -335,6 +335,26 @@ xmoe_status xmoe_expert_ffn_bwd(const void *xs, const void *w1, const void *w3, 
 xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void *h13,
                                      xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                      int64_t rows, int32_t d, int32_t h, void *dh13, void *stream);
+/*
+ * xmoe_expert_ffn_bwd_dact fed by the upstream gradient itself
+ * ("5.4 MoE模型在分布式训练中的应用", section 训练流程: the reverse path runs
+ * from the layer output back through the weighted combine into the experts;
+ * X-MoE article, section 2.1.2: the PFT's token_ids name each row's source
+ * token and combine_weights its gate weight):
+ *   dA[r] = row_weights[r] * (dy[token_ids[r]] . w2[e]^T),  then dH1, dH3 as _dact
+ * The combine backward's dye rows (w_r * dy[t]) are thus never materialised;
+ * the weight multiplies the fp32 product instead of being rounded into dye
+ * first, so results agree with xmoe_combine_bwd + xmoe_expert_ffn_bwd_dact to
+ * rounding, not bitwise.  dy [T,d]; token_ids: DEVICE int32 [rows] with values
+ * in [0, T); row_weights: DEVICE fp32 [rows] (the PFT's token_ids and
+ * combine_weights).  Limits as xmoe_expert_ffn_bwd_dact, plus T * d * element
+ * size < 2^31 bytes.
+ */
+xmoe_status xmoe_expert_ffn_bwd_dact_gather(const void *dy, const int32_t *token_ids,
+                                            const float *row_weights, const void *w2, const void *h13,
+                                            xmoe_dtype dtype, const int32_t *expert_offsets,
+                                            int32_t E, int64_t T, int64_t rows, int32_t d, int32_t h,
+                                            void *dh13, void *stream);
 xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3,
                                    xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E,
                                    int64_t rows, int32_t d, int32_t h, void *dxs, int32_t accumulate,

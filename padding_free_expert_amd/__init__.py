@@ -21,7 +21,7 @@ __all__ = [
     "xmoe_build_pft_shared", "xmoe_dispatch", "xmoe_expert_ffn_up",
     "xmoe_expert_ffn_down", "xmoe_expert_ffn", "xmoe_expert_ffn_up_gather", "xmoe_expert_ffn_gather",
     "xmoe_combine", "xmoe_combine_bwd",
-    "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13", "xmoe_expert_ffn_bwd_dw13_gather",
+    "xmoe_expert_ffn_bwd", "xmoe_expert_ffn_bwd_dact", "xmoe_expert_ffn_bwd_dact_gather", "xmoe_expert_ffn_bwd_dx", "xmoe_expert_ffn_bwd_dw13", "xmoe_expert_ffn_bwd_dw13_gather",
     "xmoe_expert_ffn_bwd_dw2", "xmoe_dispatch_bwd", "xmoe_route_bwd_workspace_size", "xmoe_route_bwd",
     "xmoe_build_pilots_workspace_size", "xmoe_build_pilots", "xmoe_ep_send_plan", "xmoe_ep_recv_plan_workspace_size",
     "xmoe_ep_recv_plan", "xmoe_scatter_rows",
@@ -77,6 +77,8 @@ _lib_combine_bwd = _sig("xmoe_combine_bwd", [_vp, _vp, ctypes.POINTER(_CPft), _i
 _lib_ffn_bwd = _sig("xmoe_expert_ffn_bwd", [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64,
                                             _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, ctypes.c_int, _i32, _vp])
 _lib_bwd_dact = _sig("xmoe_expert_ffn_bwd_dact", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp])
+_lib_bwd_dact_g = _sig("xmoe_expert_ffn_bwd_dact_gather",
+                       [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp])
 _lib_bwd_dx = _sig("xmoe_expert_ffn_bwd_dx", [_vp, _vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _i32,
                                               _vp])
 _lib_bwd_dw13 = _sig("xmoe_expert_ffn_bwd_dw13", [_vp, _vp, ctypes.c_int, _vp, _i32, _i64, _i32, _i32, _vp, _vp,
@@ -319,6 +321,15 @@ def xmoe_expert_ffn_bwd_dact(dye, w2, h13, expert_offsets, dh13, stream=None):
     E, h, _ = w2.shape
     _check(_lib_bwd_dact(_ptr(dye), _ptr(w2), _ptr(h13), _dt(dye), _ptr(expert_offsets), E, rows, d, h, _ptr(dh13),
                          _stream(stream)), "xmoe_expert_ffn_bwd_dact")
+
+
+def xmoe_expert_ffn_bwd_dact_gather(dy, token_ids, row_weights, w2, h13, expert_offsets, dh13, stream=None):
+    T, d = dy.shape
+    E, h, _ = w2.shape
+    rows = token_ids.shape[0]
+    _check(_lib_bwd_dact_g(_ptr(dy), _ptr(token_ids), _ptr(row_weights), _ptr(w2), _ptr(h13), _dt(dy),
+                           _ptr(expert_offsets), E, T, rows, d, h, _ptr(dh13), _stream(stream)),
+           "xmoe_expert_ffn_bwd_dact_gather")
 
 
 def xmoe_expert_ffn_bwd_dx(dh13, w1, w3, expert_offsets, dxs, accumulate=False, stream=None):

@@ -401,8 +401,24 @@ xmoe_status xmoe_expert_ffn_bwd_dact(const void *dye, const void *w2, const void
     REQUIRE(aligned16(dye) && aligned16(w2) && aligned16(h13) && aligned16(dh13), XMOE_ERR_UNSUPPORTED,
             "matrices must be 16-byte aligned");
     CHECK_DEVICE();
-    return hip_status(xmoe::launch_ffn_bwd_dact(dtype, dye, w2, h13, expert_offsets, E, rows, d, h, dh13, S(stream)),
+    return hip_status(xmoe::launch_ffn_bwd_dact(dtype, dye, nullptr, 0, nullptr, w2, h13, expert_offsets, E, rows, d, h,
+                                                dh13, S(stream)),
                       "xmoe_expert_ffn_bwd_dact launch");
+}
+
+xmoe_status xmoe_expert_ffn_bwd_dact_gather(const void *dy, const int32_t *token_ids, const float *row_weights,
+                                            const void *w2, const void *h13, xmoe_dtype dtype,
+                                            const int32_t *expert_offsets, int32_t E, int64_t T, int64_t rows,
+                                            int32_t d, int32_t h, void *dh13, void *stream) {
+    TRY(check_dtype(dtype));
+    REQUIRE(w2 && (rows == 0 || (row_weights && h13 && dh13)), XMOE_ERR_INVALID_VALUE, "a required pointer is NULL");
+    TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
+    TRY(check_gather(dy, token_ids, T, rows, d, dtype));
+    REQUIRE(aligned16(w2) && aligned16(h13) && aligned16(dh13), XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
+    CHECK_DEVICE();
+    return hip_status(xmoe::launch_ffn_bwd_dact(dtype, dy, token_ids, T, row_weights, w2, h13, expert_offsets, E, rows,
+                                                d, h, dh13, S(stream)),
+                      "xmoe_expert_ffn_bwd_dact_gather launch");
 }
 
 xmoe_status xmoe_expert_ffn_bwd_dx(const void *dh13, const void *w1, const void *w3, xmoe_dtype dtype,

@@ -16,7 +16,9 @@
 //   up       act = silu(xs.W1) * (xs.W3)        A = xs, B = W1 | W3 (n-contiguous);
 //                                               or A row r = x[token_ids[r]] (gather fused)
 //   down     ye  = act.W2                       A = act, B = W2 (n-contiguous)
-//   dgrad2   dA  = dye.W2^T -> dH1, dH3         A = dye, B = W2 read k-contiguous
+//   dgrad2   dA  = dye.W2^T -> dH1, dH3         A = dye, B = W2 read k-contiguous;
+//                                               or A row r = dy[token_ids[r]] and dA
+//                                               row r scaled by the combine weight
 //   dgrad1   dxs = dH1.W1^T + dH3.W3^T          two k phases, B read k-contiguous
 //   wgrad13  dW1 = xs^T dH1, dW3 = xs^T dH3     reduction over the expert's rows
 //   wgrad2   dW2 = act^T dye                    reduction over the expert's rows
@@ -151,8 +153,11 @@ hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_
                : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, bf16_t, 2>(p, s);
 }
 
-// dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13
-hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const void *h13, const int32_t *offsets, int E,
+// dA = dye . W2[e]^T with the SwiGLU backward in the epilogue -> dh13; with
+// row_map, A row r is dye[row_map[r]] (dye then has map_rows rows), and with
+// row_scale dA row r is multiplied by row_scale[r] before the SwiGLU backward
+hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const int32_t *row_map, int64_t map_rows,
+                               const float *row_scale, const void *w2, const void *h13, const int32_t *offsets, int E,
                                int64_t rows, int d, int h, void *dh13, hipStream_t s) {
     const int64_t dh = static_cast<int64_t>(d) * h;
     hipError_t err;
@@ -160,6 +165,9 @@ hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const vo
     p.N = h;
     p.K = d;
     p.A0 = dye;
+    p.a_map = row_map;
+    p.a_map_rows = map_rows;
+    p.row_scale = row_scale;
     p.lda = d;
     p.B0 = w2;          // B(k=c, n=j) = W2[e][j*d + c]
     p.ldb = d;
@@ -285,7 +293,7 @@ hipError_t launch_ffn_bwd(int dt, const void *xs, const void *w1, const void *w3
                           const void *h13, const void *dye, const int32_t *offsets, int E, int64_t rows, int d, int h,
                           void *dh13, void *dxs, bool accumulate_dxs, void *dw1, void *dw3, void *dw2, int grad_dt,
                           bool accumulate_dw, hipStream_t s) {
-    hipError_t err = launch_ffn_bwd_dact(dt, dye, w2, h13, offsets, E, rows, d, h, dh13, s);
+    hipError_t err = launch_ffn_bwd_dact(dt, dye, nullptr, 0, nullptr, w2, h13, offsets, E, rows, d, h, dh13, s);
     if (err == hipSuccess) err = launch_ffn_bwd_dx(dt, dh13, w1, w3, offsets, E, rows, d, h, dxs, accumulate_dxs, s);
     if (err == hipSuccess)
         err = launch_ffn_bwd_dw13(dt, xs, nullptr, 0, dh13, offsets, E, rows, d, h, dw1, dw3, grad_dt, accumulate_dw, s);

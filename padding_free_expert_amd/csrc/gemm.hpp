@@ -46,6 +46,10 @@ struct GemmArgs {
     void *C0, *Cx;
     int64_t ldc, c_gstride;
     const void *aux;         // EPI_SWIGLU_BWD: saved [H1|H3]
+    // EPI_SWIGLU_BWD (optional): dA of rows-space row r is multiplied by
+    // row_scale[r] before the SwiGLU backward (the combine weight of a row
+    // whose A operand is the unweighted upstream gradient)
+    const float *row_scale;
     void *aux_out;           // EPI_SWIGLU: [H1|H3] to save (optional)
     int64_t ld_aux;
     int hoff;                // column offset of the H3 half in [H1|H3]
@@ -111,9 +115,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, int64_t cbase_row, i
         const float h1 = Elem<OutT>::load(s, row * p.ld_aux + n);
         const float h3 = Elem<OutT>::load(s, row * p.ld_aux + p.hoff + n);
         const float sg = 1.0f / (1.0f + __expf(-h1));
+        const float da = p.row_scale ? v0 * p.row_scale[row] : v0;
         OutT *o = static_cast<OutT *>(p.C0);
-        Elem<OutT>::store(o, row * p.ldc + n, v0 * h3 * sg * (1.0f + h1 * (1.0f - sg)));
-        Elem<OutT>::store(o, row * p.ldc + p.hoff + n, v0 * h1 * sg);
+        Elem<OutT>::store(o, row * p.ldc + n, da * h3 * sg * (1.0f + h1 * (1.0f - sg)));
+        Elem<OutT>::store(o, row * p.ldc + p.hoff + n, da * h1 * sg);
     } else {  // EPI_ROUTER: s = z * scale (+ bias[n]), each an IEEE fp32 operation
         float s = __fmul_rn(v0, p.scale);
         if (p.col_bias) s = __fadd_rn(s, p.col_bias[n]);
@@ -383,16 +388,18 @@ __device__ __forceinline__ void epilogue4(const GemmArgs &p, int64_t crow, int64
                 *reinterpret_cast<bf4 *>(s) = pack(v0);
                 *reinterpret_cast<bf4 *>(s + p.hoff) = pack(v1);
             }
-        } else {  // EPI_SWIGLU_BWD: v0 = dA
+        } else {  // EPI_SWIGLU_BWD: v0 = dA (times the row's scale, if any)
             const __bf16 *s = static_cast<const __bf16 *>(p.aux) + row * p.ld_aux + n;
             float h1[4], h3[4], g1[4], g3[4];
             unpack(*reinterpret_cast<const bf4 *>(s), h1);
             unpack(*reinterpret_cast<const bf4 *>(s + p.hoff), h3);
+            const float rs = p.row_scale ? p.row_scale[row] : 1.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[i]));
-                g1[i] = v0[i] * h3[i] * sg * (1.0f + h1[i] * (1.0f - sg));
-                g3[i] = v0[i] * h1[i] * sg;
+                const float da = v0[i] * rs;
+                g1[i] = da * h3[i] * sg * (1.0f + h1[i] * (1.0f - sg));
+                g3[i] = da * h1[i] * sg;
             }
             *reinterpret_cast<bf4 *>(C0 + row * p.ldc + n) = pack(g1);
             *reinterpret_cast<bf4 *>(C0 + row * p.ldc + p.hoff + n) = pack(g3);
@@ -684,6 +691,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, const Tile &t, 
             make_rsrc(rsrc_base + (EPI == EPI_ACCUM ? q.coff : 0) + (q.crow + m0) * ld_in,
                       static_cast<int64_t>(t.Mg - m0) * ld_in * 2);
         __bf16 *dst = static_cast<__bf16 *>(p.C0) + q.coff + q.crow * p.ldc;
+        // SwiGLU backward with row scales: a lane's rows are m_lane + 32 i
+        // (each wave combines its own rows, in pass wm / WPP); multiplying by
+        // 1 where there is no scale leaves dA exact
+        float rsc[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m_lane + i * 32;
+            rsc[i] = (EPI == EPI_SWIGLU_BWD && p.row_scale && m < t.Mg) ? p.row_scale[q.crow + m] : 1.0f;
+        }
         __syncthreads();  // every wave is done with the ring
         for (int pass = 0; pass < kPass; ++pass) {
 #pragma unroll
@@ -718,7 +734,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, const Tile &t, 
                                 f4_t g1, g3;
 #pragma unroll
                                 for (int r = 0; r < 4; ++r) {
-                                    const float v0 = acc[0][i][j][4 * g + r];
+                                    const float v0 = acc[0][i][j][4 * g + r] * rsc[i];
                                     const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h1[r]));
                                     g1[r] = v0 * h3[r] * sg * (1.0f + h1[r] * (1.0f - sg));
                                     g3[r] = v0 * h1[r] * sg;

@@ -77,7 +77,10 @@ hipError_t launch_ffn_up(int dt, const void *xs, const int32_t *row_map, int64_t
 hipError_t launch_ffn_down(int dt, const void *act, const void *w2, const int32_t *offsets, int E, int64_t rows,
                            int d, int h, void *ye, bool accumulate, hipStream_t s);
 // the four products of the expert backward, each on its own stream if the caller wants
-hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const void *w2, const void *h13, const int32_t *offsets, int E,
+// row_map (may be nullptr): A row r is dye[row_map[r]] (dye has map_rows rows);
+// row_scale (may be nullptr): dA row r times row_scale[r] before the SwiGLU backward
+hipError_t launch_ffn_bwd_dact(int dt, const void *dye, const int32_t *row_map, int64_t map_rows,
+                               const float *row_scale, const void *w2, const void *h13, const int32_t *offsets, int E,
                                int64_t rows, int d, int h, void *dh13, hipStream_t s);
 hipError_t launch_ffn_bwd_dx(int dt, const void *dh13, const void *w1, const void *w3, const int32_t *offsets, int E,
                              int64_t rows, int d, int h, void *dxs, bool accumulate, hipStream_t s);

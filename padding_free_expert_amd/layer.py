@@ -14,7 +14,7 @@ import torch
 
 from . import (PFT, xmoe_build_pft, xmoe_build_pft_shared, xmoe_build_pft_workspace_size, xmoe_combine,
                xmoe_combine_bwd, xmoe_dispatch_bwd, xmoe_expert_ffn_bwd,
-               xmoe_expert_ffn_bwd_dact, xmoe_expert_ffn_bwd_dw13_gather, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx,
+               xmoe_expert_ffn_bwd_dact_gather, xmoe_expert_ffn_bwd_dw13_gather, xmoe_expert_ffn_bwd_dw2, xmoe_expert_ffn_bwd_dx,
                xmoe_expert_ffn_down, xmoe_expert_ffn_up, xmoe_expert_ffn_up_gather, xmoe_route, xmoe_route_bwd,
                xmoe_route_bwd_workspace_size, xmoe_route_workspace_size)
 
@@ -216,8 +216,17 @@ class PaddingFreeMoE:
                                 self.sh_dx, self._ds1, self._ds3, self._ds2, stream=side)
             if side is main:
                 mark("shared_ffn_bwd")
-        xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w_all, stream=main)
-        mark("combine_bwd")
+        off = self.pft.expert_offsets
+        ws = self.wside if self.overlap else main
+        # dA reads dy through the PFT and applies each row's combine weight
+        # itself, so it does not wait for the combine backward, which runs
+        # beside it on the weight-gradient stream: its dye feeds dW2 there and
+        # its dtopk_w the gate's backward
+        if ws is not main:
+            ws.wait_stream(main)
+        xmoe_combine_bwd(dy, self.ye, self.pft, self.dye, self.dtopk_w_all, stream=ws)
+        if ws is main:
+            mark("combine_bwd")
         # the gate's backward needs only the routed slots' dtopk_w, the logits
         # and x: it runs beside the expert backward.  With unmerged shared
         # experts it adds dz . wg^T into their dx; otherwise it writes its own
@@ -225,27 +234,29 @@ class PaddingFreeMoE:
         rdst = self.sh_dx if self.side_shared else self.rdx
         if self.side_shared:
             gs = side
-        gs.wait_stream(main)
+        if gs is not ws:
+            gs.wait_stream(ws)
         xmoe_route_bwd(self.x, w["wg"], self.logits, self.topk_ids, self.dtopk_w, rdst, self.dwg,
                        self.rbwd_ws, self.inv_tau, accumulate=self.side_shared, stream=gs)
         if gs is main:
             mark("route_bwd")
         dx_add = rdst
         if self.lean:
-            # recompute the pre-activations (act is rewritten with the same values)
+            # recompute the pre-activations (act is rewritten with the same
+            # values; dW2 reads act only after this)
             xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, self.W1, self.W3, self.pft.expert_offsets,
                                       self.act, self.h13, stream=main)
             mark("recompute_h13")
-        off = self.pft.expert_offsets
-        ws = self.wside if self.overlap else main
+            if ws is not main:
+                ws.wait_stream(main)
+        xmoe_expert_ffn_bwd_dact_gather(dy, self.pft.token_ids, self.pft.combine_weights, self.W2, self.h13, off,
+                                        self.dh13, stream=main)
+        mark("bwd_dact")
         # weight gradients: dW2 needs act and dye only; dW1/dW3 need dH1/dH3 and
         # the token rows, gathered through the PFT inside their loads
-        ws.wait_stream(main)
         xmoe_expert_ffn_bwd_dw2(self.act, self.dye, off, self.dW2, stream=ws)
         if ws is main:
             mark("bwd_dw2")
-        xmoe_expert_ffn_bwd_dact(self.dye, self.W2, self.h13, off, self.dh13, stream=main)
-        mark("bwd_dact")
         w13 = main if self.dw13_main else ws
         if w13 is not main:
             w13.wait_stream(main)

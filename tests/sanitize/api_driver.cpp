@@ -80,6 +80,11 @@ int main() {
            XMOE_ERR_UNSUPPORTED);
     EXPECT_DEVICE(xmoe_expert_ffn_bwd(p, p, p, p, p, p, p, bf, ip, 4, 100, 64, 64, p, p, 1, p, p, p, f32, 1, nullptr));
     EXPECT_DEVICE(xmoe_expert_ffn_bwd_dact(p, p, p, bf, ip, 4, 100, 64, 64, p, nullptr));
+    EXPECT(xmoe_expert_ffn_bwd_dact_gather(p, ip, nullptr, p, p, bf, ip, 4, 100, 100, 64, 64, p, nullptr),
+           XMOE_ERR_INVALID_VALUE);
+    EXPECT(xmoe_expert_ffn_bwd_dact_gather(p, ip, fp, p, p, bf, ip, 4, int64_t{1} << 17, 100, 8192, 64, p, nullptr),
+           XMOE_ERR_UNSUPPORTED);
+    EXPECT_DEVICE(xmoe_expert_ffn_bwd_dact_gather(p, ip, fp, p, p, bf, ip, 4, 100, 100, 64, 64, p, nullptr));
     EXPECT_DEVICE(xmoe_expert_ffn_bwd_dx(p, p, p, bf, ip, 4, 100, 64, 64, p, 1, nullptr));
     EXPECT(xmoe_expert_ffn_bwd_dw13(p, p, bf, ip, 4, 100, 64, 64, p, p, static_cast<xmoe_dtype>(9), 0, nullptr),
            XMOE_ERR_UNSUPPORTED);

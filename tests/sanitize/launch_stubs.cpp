@@ -43,8 +43,8 @@ hipError_t launch_ffn_up(int, const void *, const int32_t *, int64_t, const void
                          int64_t, int, int, void *, void *, hipStream_t) { return hipSuccess; }
 hipError_t launch_ffn_down(int, const void *, const void *, const int32_t *, int, int64_t, int, int, void *, bool,
                            hipStream_t) { return hipSuccess; }
-hipError_t launch_ffn_bwd_dact(int, const void *, const void *, const void *, const int32_t *, int, int64_t, int, int,
-                               void *, hipStream_t) { return hipSuccess; }
+hipError_t launch_ffn_bwd_dact(int, const void *, const int32_t *, int64_t, const float *, const void *, const void *,
+                               const int32_t *, int, int64_t, int, int, void *, hipStream_t) { return hipSuccess; }
 hipError_t launch_ffn_bwd_dx(int, const void *, const void *, const void *, const int32_t *, int, int64_t, int, int,
                              void *, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_ffn_bwd_dw13(int, const void *, const int32_t *, int64_t, const void *, const int32_t *, int, int64_t,

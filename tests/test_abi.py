@@ -106,6 +106,21 @@ def test_shared_buffer_and_route_bwd_reject_on_host(xm):
     assert xm._lib_rbwd(p, p, p, p, p, 3, 1, 100, 64, 64, 6, 1.0, 1, p, p, p, 1 << 24, None) == 1
 
 
+def test_gathered_dact_rejects_on_host(xm):
+    p = ctypes.c_void_p(16)  # never dereferenced
+    f = xm._lib_bwd_dact_g
+    # dy [T, d] of 2^31 bytes or more cannot be gathered through one buffer
+    assert f(p, p, p, p, p, 1, p, 4, 1 << 17, 100, 8192, 64, p, None) == 2
+    # NULL dy or token_ids with rows to gather; NULL row weights
+    assert f(None, p, p, p, p, 1, p, 4, 100, 100, 64, 64, p, None) == 1
+    assert f(p, None, p, p, p, 1, p, 4, 100, 100, 64, 64, p, None) == 1
+    assert f(p, p, None, p, p, 1, p, 4, 100, 100, 64, 64, p, None) == 1
+    # h not a multiple of 8, misaligned dy
+    assert f(p, p, p, p, p, 1, p, 4, 100, 100, 64, 12, p, None) == 2
+    assert f(ctypes.c_void_p(18), p, p, p, p, 1, p, 4, 100, 100, 64, 64, p, None) == 2
+    assert xm._lib_last_error() != b""
+
+
 def test_gathered_wgrad_rejects_on_host(xm):
     p = ctypes.c_void_p(16)  # never dereferenced
     f = xm._lib_bwd_dw13_g

@@ -431,6 +431,68 @@ def test_expert_ffn_bwd_dw13_gather(xm, dtype, T, d, h, E, k, skew):
     assert_wgrad_close(host(dw3), ref["dw3"], rows, lambda e: floors(e)[1], rt, "dw3")
 
 
+# the gathered dA: the gather cases plus 1300 rows per expert
+DACT_GATHER_CASES = GATHER_CASES + [("bf16", 2600, 192, 136, 4, 2, 0.5)]
+
+
+@pytest.mark.parametrize("dtype,T,d,h,E,k,skew", DACT_GATHER_CASES)
+def test_expert_ffn_bwd_dact_gather(xm, dtype, T, d, h, E, k, skew):
+    """dA straight from the upstream gradient: row r reads dy[token_ids[r]] and
+    its product is scaled by the row's combine weight before the SwiGLU
+    backward.  Against the oracle's combine backward (dye = w * dy[token],
+    unrounded) followed by its expert backward, and against the two-call GPU
+    path, which rounds dye to the input dtype first."""
+    ids, w = workloads.random_topk(T, E, k, seed=T + 5 * d, skew=skew)
+    ref_pft = orc.build_pft(ids.numpy(), w.numpy(), E)
+    tok, off, cw = ref_pft["token_ids"], ref_pft["expert_offsets"], ref_pft["combine_weights"]
+    R = T * k
+    row_expert = np.repeat(np.arange(E, dtype=np.int32), np.diff(off))
+    x = workloads.random_rows(T, d, dtype, seed=T + 21)
+    dy = workloads.random_rows(T, d, dtype, seed=T + 22)
+    g = torch.Generator().manual_seed(T + 2 * h)
+    tdt = DT[dtype]
+    w1 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w3 = (torch.randn((E, d, h), generator=g) / d ** 0.5).to(tdt)
+    w2 = (torch.randn((E, h, d), generator=g) / h ** 0.5).to(tdt)
+    c = lambda t: t.cuda()
+    tok_d, off_d = torch.from_numpy(tok).cuda(), torch.from_numpy(off).cuda()
+    cw_d = torch.from_numpy(cw.astype(np.float32)).cuda()
+    act = torch.empty((R, h), dtype=tdt, device="cuda")
+    h13 = torch.empty((R, 2 * h), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_up_gather(c(x), tok_d, c(w1), c(w3), off_d, act, h13)
+    dh13 = torch.full((R, 2 * h), float("nan"), dtype=tdt, device="cuda")   # must be fully overwritten
+    xm.xmoe_expert_ffn_bwd_dact_gather(c(dy), tok_d, cw_d, c(w2), h13, off_d, dh13)
+    # the oracle: the combine backward's dye (not rounded), then the expert backward
+    fwd = orc.ffn(orc_in(x), row_expert, orc_in(w1), orc_in(w3), orc_in(w2), row_token=tok, want_hidden=True)
+    dye = orc.combine_bwd(orc_in(dy), fwd["ye"], tok, cw)["dye"]
+    ref = orc.ffn_bwd(orc_in(x), row_expert, orc_in(w1), orc_in(w3), orc_in(w2), dye, row_token=tok,
+                      want_dh=True, want_dw=False)
+    rt = RTOL[dtype]
+    got = host(dh13)
+    assert_close(got[:, :h], ref["dh1"], rt, "dh1")
+    assert_close(got[:, h:], ref["dh3"], rt, "dh3")
+    # the two-call path: dye = w * dy[token] rounded to the input dtype, then dA
+    dye_d = torch.empty((R, d), dtype=tdt, device="cuda")
+    dtw = torch.empty(R, dtype=torch.float32, device="cuda")
+    pft = xm.PFT(T, E, k)
+    for name, t in pft.fields().items():
+        t.copy_(torch.from_numpy(ref_pft[name]))
+    ye = torch.empty((R, d), dtype=tdt, device="cuda")
+    xm.xmoe_expert_ffn_down(act, c(w2), off_d, ye)
+    xm.xmoe_combine_bwd(c(dy), ye, pft, dye_d, dtw)
+    dh13b = torch.empty_like(dh13)
+    xm.xmoe_expert_ffn_bwd_dact(dye_d, c(w2), h13, off_d, dh13b)
+    torch.cuda.synchronize()
+    # the two-call path rounds w * dy to the input dtype before the product,
+    # which moves elements where the product cancels by several ulps; the
+    # gathered path scales the fp32 product, so it is at least as close
+    ref_dh = np.concatenate([ref["dh1"], ref["dh3"]], 1)
+    rms = float(np.sqrt(np.mean(ref_dh * ref_dh))) if ref_dh.size else 0.0
+    worst = lambda a: float(np.max(np.abs(a - ref_dh) / (np.abs(ref_dh) + rms))) if ref_dh.size else 0.0
+    e_new, e_old = worst(got), worst(host(dh13b))
+    assert e_new <= 1.05 * e_old + 1e-6, (e_new, e_old)
+
+
 def test_gathered_reads_outside_x_are_zero(xm):
     """bf16 gathers read x through a bounds-checked buffer: a token id past T
     or negative reads a zero row, in the up-projection and in dW1/dW3 alike
