@@ -427,7 +427,8 @@ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255);
 // product (T x d times d x E) still gives each compute unit a block; the
 // partial sums land in the workspace and the top-k kernel adds them in order.
 // (Aiming at two blocks per compute unit doubles the partial sums written and
-// read again, and measured 4-10% slower at 128-256 experts.)
+// read again: 4-10% slower at 128-256 experts with 32-deep k blocks, 14-25%
+// slower with the 64-deep ones, which fit one block per compute unit.)
 int route_kparts(int64_t T, int d, int E) {
     const int bn = col_tile(E);
     const int64_t tiles = ((T + 127) / 128) * ((E + bn - 1) / bn);
@@ -489,13 +490,18 @@ hipError_t launch_route(int dt, const void *x, const void *wg, int64_t T, int d,
         p.kparts = kparts;
         p.kpart_len = ((d / kparts + 31) / 32) * 32;
         p.c_gstride = T * E;
+        // 64-deep k blocks: each x row then brings whole 128-byte lines per
+        // block (half lines with 32), one block per compute unit.  Alone, 32768
+        // tokens of d = 4096 at 160 experts 115.6 -> 101.6 us (route with its
+        // top-k), 8192 of d = 7168 at 256 experts 61.0 -> 58.5 us, 16384 of
+        // d = 2048 at 128 experts 38.8 -> 37.5 us; bitwise the same logits
         switch (col_tile(E)) {
-            case 128: err = launch_gemm_dma<128, 128, 32, 2, 2, 1, true, false, 4, EPI_STORE, float, 2>(p, s); break;
+            case 128: err = launch_gemm_dma<128, 128, 64, 2, 2, 1, true, false, 3, EPI_STORE, float, 1>(p, s); break;
             // E <= 192: four waves side by side over the 256 columns, so the
             // wave whose 64 columns all lie past E skips its products
             default:
-                err = E <= 192 ? launch_gemm_dma<128, 256, 32, 1, 4, 1, true, false, 3, EPI_STORE, float, 2>(p, s)
-                               : launch_gemm_dma<128, 256, 32, 2, 2, 1, true, false, 3, EPI_STORE, float, 2>(p, s);
+                err = E <= 192 ? launch_gemm_dma<128, 256, 64, 1, 4, 1, true, false, 3, EPI_STORE, float, 1>(p, s)
+                               : launch_gemm_dma<128, 256, 64, 2, 2, 1, true, false, 3, EPI_STORE, float, 1>(p, s);
                 break;
         }
     } else {
