@@ -202,6 +202,8 @@ xmoe_status xmoe_dispatch(const void *x, xmoe_dtype dtype, int64_t T, int32_t d,
  *   H1 = xs[r] . w1[e],  H3 = xs[r] . w3[e]   (w1, w3 [E,d,h])
  *   act[r] = silu(H1) * H3,  silu(a) = a / (1 + exp(-a))           (act [rows,h])
  *   h13[r] = [H1 | H3] rounded to the dtype, if h13 != NULL       (h13 [rows,2h])
+ * act may be NULL when h13 is given: only the pre-activations are written (as
+ * when a backward recomputes them instead of keeping them).
  * expert_offsets: DEVICE int32 [E+1], non-decreasing, offsets[0] == 0,
  * offsets[E] == rows (segments are clamped to [0, rows]).  The launch is sized
  * on the host from `rows` and E alone; the tile scheduler reads the offsets on

@@ -269,7 +269,8 @@ xmoe_status xmoe_expert_ffn_up(const void *xs, const void *w1, const void *w3, x
                                const int32_t *expert_offsets, int32_t E, int64_t rows, int32_t d, int32_t h, void *act,
                                void *h13, void *stream) {
     TRY(check_dtype(dtype));
-    REQUIRE(w1 && w3 && (rows == 0 || (xs && act)), XMOE_ERR_INVALID_VALUE, "xs, w1, w3 and act are required");
+    REQUIRE(w1 && w3 && (rows == 0 || (xs && (act || h13))), XMOE_ERR_INVALID_VALUE,
+            "xs, w1, w3 and act or h13 are required");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     REQUIRE(aligned16(xs) && aligned16(w1) && aligned16(w3) && aligned16(act) && aligned16(h13),
             XMOE_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
@@ -297,7 +298,7 @@ xmoe_status xmoe_expert_ffn_up_gather(const void *x, const int32_t *token_ids, c
                                       xmoe_dtype dtype, const int32_t *expert_offsets, int32_t E, int64_t T,
                                       int64_t rows, int32_t d, int32_t h, void *act, void *h13, void *stream) {
     TRY(check_dtype(dtype));
-    REQUIRE(w1 && w3 && (rows == 0 || act), XMOE_ERR_INVALID_VALUE, "w1, w3 and act are required");
+    REQUIRE(w1 && w3 && (rows == 0 || act || h13), XMOE_ERR_INVALID_VALUE, "w1, w3 and act or h13 are required");
     TRY(check_ffn_sizes(expert_offsets, E, rows, d, h));
     TRY(check_gather(x, token_ids, T, rows, d, dtype));
     REQUIRE(aligned16(w1) && aligned16(w3) && aligned16(act) && aligned16(h13), XMOE_ERR_UNSUPPORTED,

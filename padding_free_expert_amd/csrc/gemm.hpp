@@ -104,7 +104,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &p, int64_t cbase_row, i
         Elem<OutT>::store(c, i, Elem<OutT>::load(c, i) + v0);
     } else if constexpr (EPI == EPI_SWIGLU) {
         // v0 = H1, v1 = H3 at the same (row, n)
-        Elem<OutT>::store(static_cast<OutT *>(p.C0), row * p.ldc + n, silu_f(v0) * v1);
+        if (p.C0) Elem<OutT>::store(static_cast<OutT *>(p.C0), row * p.ldc + n, silu_f(v0) * v1);
         if (p.aux_out) {
             OutT *s = static_cast<OutT *>(p.aux_out);
             Elem<OutT>::store(s, row * p.ld_aux + n, v0);
@@ -382,7 +382,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs &p, int64_t crow, int64
                 const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-v0[i]));
                 a[i] = v0[i] * sg * v1[i];
             }
-            *reinterpret_cast<bf4 *>(C0 + row * p.ldc + n) = pack(a);
+            if (C0) *reinterpret_cast<bf4 *>(C0 + row * p.ldc + n) = pack(a);
             if (p.aux_out) {
                 __bf16 *s = static_cast<__bf16 *>(p.aux_out) + row * p.ld_aux + n;
                 *reinterpret_cast<bf4 *>(s) = pack(v0);
@@ -607,9 +607,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, const Tile &t, 
         typedef __bf16 bf4_t __attribute__((ext_vector_type(4)));
         typedef float f4_t __attribute__((ext_vector_type(4)));
         __bf16 *cs = reinterpret_cast<__bf16 *>(smem);
+        // EPI_SWIGLU outputs: act (0) unless C0 is null, H1 and H3 (1, 2) if saved
+        const int o0 = (EPI == EPI_SWIGLU && p.C0 == nullptr) ? 1 : 0;
         const int nout = EPI == EPI_SWIGLU ? (p.aux_out ? 3 : 1) : ((NB == 2 && p.Cx) ? 2 : 1);
         __syncthreads();  // every wave is done with the ring
-        for (int o = 0; o < nout; ++o) {
+        for (int o = o0; o < nout; ++o) {
             __bf16 *dst;
             int64_t ld;
             if constexpr (EPI == EPI_SWIGLU) {

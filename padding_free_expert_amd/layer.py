@@ -209,7 +209,7 @@ class PaddingFreeMoE:
             side.wait_stream(main)
             s1, s3, s2 = self._shared_w()
             if self.lean:
-                xmoe_expert_ffn_up(self.x, s1, s3, self.sh_off, self.sh_act, self.sh_h13, stream=side)
+                xmoe_expert_ffn_up(self.x, s1, s3, self.sh_off, None, self.sh_h13, stream=side)
                 if side is main:
                     mark("recompute_shared_h13")
             xmoe_expert_ffn_bwd(self.x, s1, s3, s2, self.sh_act, self.sh_h13, dy, self.sh_off, self.sh_dh13,
@@ -242,13 +242,10 @@ class PaddingFreeMoE:
             mark("route_bwd")
         dx_add = rdst
         if self.lean:
-            # recompute the pre-activations (act is rewritten with the same
-            # values; dW2 reads act only after this)
+            # recompute the pre-activations only (act is kept from the forward)
             xmoe_expert_ffn_up_gather(self.x, self.pft.token_ids, self.W1, self.W3, self.pft.expert_offsets,
-                                      self.act, self.h13, stream=main)
+                                      None, self.h13, stream=main)
             mark("recompute_h13")
-            if ws is not main:
-                ws.wait_stream(main)
         xmoe_expert_ffn_bwd_dact_gather(dy, self.pft.token_ids, self.pft.combine_weights, self.W2, self.h13, off,
                                         self.dh13, stream=main)
         mark("bwd_dact")

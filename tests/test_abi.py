@@ -69,6 +69,8 @@ def test_invalid_arguments_rejected_on_host(xm):
     assert xm._lib_up(p, p, p, 1, p, 4, 100, 64, 12, p, None, None) == 2
     assert xm._lib_up(p, p, p, 1, p, 0, 100, 64, 64, p, None, None) == 1
     assert xm._lib_up(p, p, p, 1, None, 4, 100, 64, 64, p, None, None) == 1
+    # neither act nor h13 to write
+    assert xm._lib_up(p, p, p, 1, p, 4, 100, 64, 64, None, None, None) == 1
     # build_pft: workspace too small
     pft = xm._CPft(16, 16, 16, 16, 16, 16)
     assert xm._lib_pft(p, p, 1000, 16, 4, ctypes.byref(pft), p, 8, None) == 3

@@ -366,6 +366,12 @@ def test_expert_ffn_gather(xm, dtype, T, d, h, E, k, skew):
     act3 = torch.empty_like(act)
     xm.xmoe_expert_ffn_up_gather(c(x), tok_d, c(w1), c(w3), off_d, act3)
     assert torch.equal(act3, act)
+    # and the pre-activations alone (no act), gathered and over xs
+    h13b, h13c = torch.full_like(h13, float("nan")), torch.full_like(h13, float("nan"))
+    xm.xmoe_expert_ffn_up_gather(c(x), tok_d, c(w1), c(w3), off_d, None, h13b)
+    xm.xmoe_expert_ffn_up(xs, c(w1), c(w3), off_d, None, h13c)
+    torch.cuda.synchronize()
+    assert torch.equal(h13b, h13) and torch.equal(h13c, h13)
 
 
 # the gathered weight gradient: ragged and empty experts, d and h off the
