@@ -35,6 +35,17 @@ def test_library_exports_every_declared_symbol(xm):
     assert not missing, missing
 
 
+def test_c_caller_links_the_library():
+    """The C program that drives the layer through the C ABI (built with the
+    library) loads libxmoe.so through its run path; without arguments it
+    prints its usage before any HIP call."""
+    import subprocess
+    exe = os.path.join(ROOT, "tests", "c_abi", "layer_c")
+    assert os.path.exists(exe), "tests/c_abi/layer_c is not built"
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr, (r.returncode, r.stderr)
+
+
 def test_workspace_queries(xm):
     import torch
     assert xm.xmoe_build_pft_workspace_size(32768, 160, 8) >= 2 * 128 * 160 * 4
