@@ -38,7 +38,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const T *__restrict__ x, 
     for (int jb = 0; jb < k; jb += 64) {
         const int nj = min(64, k - jb);
         const int r_lane = lane < nj ? s2r[t * k + jb + lane] : -1;
-        for (int c0 = lane; c0 < nvec; c0 += 64 * kUnroll) {
+        // the trip count is the same for every lane: each lane must be active
+        // when the others read its slot row with a shuffle (a read from an
+        // inactive lane does not return that lane's value)
+        for (int cb = 0; cb < nvec; cb += 64 * kUnroll) {
+            const int c0 = cb + lane;
             uint4 v[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -69,7 +73,10 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const T *__restrict__ s
     const int lane = threadIdx.x & 63;
     constexpr int V = Elem<T>::kVec;
     const int nvec = d / V;
-    for (int c0 = lane; c0 < nvec; c0 += 64 * kUnroll) {
+    // a wave-uniform trip count, as in the dispatch: every lane loads its slot
+    // and takes part in the shuffles, also where d / V < k
+    for (int cb = 0; cb < nvec; cb += 64 * kUnroll) {
+        const int c0 = cb + lane;
         float acc[kUnroll][V];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)

@@ -82,6 +82,46 @@ def test_layer_degenerate(xm, wl):
     check_layer(xm, wl, inp, f"layer {wl.name}")
 
 
+def _random_layers(n: int, seed: int):
+    """Seeded layer shapes drawn across the limits the boundary states:
+    widths that are multiples of 8 but rarely of a tile, experts per token up
+    to E, bf16 expert counts that are multiples of 8 (any count in fp32),
+    shared experts, Zipf-skewed or select-biased routing, a logit scale, and
+    the lean and merged layer variants.  Sizes keep the fp64 oracle to
+    seconds per case."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        dt = "f32" if i % 4 == 3 else "bf16"
+        E = int(rs.randint(1, 21)) * 8 if dt == "bf16" else int(rs.randint(1, 41))
+        k = int(rs.randint(1, min(E, 8) + 1))
+        T = int(rs.choice([1, 2, 3, 7, 33, 100, 257, 511, 700, 1031, 1500]))
+        d = 8 * int(rs.randint(1, 81))
+        h = 8 * int(rs.randint(1, 65))
+        ns = int(rs.randint(0, 3))
+        hs = h * int(rs.randint(1, 3)) if ns and rs.rand() < 0.5 else (8 * int(rs.randint(1, 33)) if ns else 0)
+        zipf = float(rs.choice([0.0, 0.0, 1.1]))
+        sbv = float(rs.choice([0.0, 0.0, 0.1]))
+        inv_tau = float(rs.choice([1.0, 1.0, 0.5, 2.0]))
+        wl = workloads.Workload(f"rand{i}", dt, T=T, d=d, E=E, h=h, k=k, n_shared=ns, h_shared=hs, inv_tau=inv_tau,
+                                select_bias_var=sbv, zipf_s=zipf, backward=True, seed=1000 + i)
+        out.append((wl, bool(rs.rand() < 0.3), bool(ns and hs % h == 0 and rs.rand() < 0.5)))
+    return out
+
+
+RANDOM_LAYERS = _random_layers(24, 2026)
+
+
+@pytest.mark.parametrize("wl,lean,merge", RANDOM_LAYERS,
+                         ids=[f"{w.name}-{w.dtype}-T{w.T}-d{w.d}-E{w.E}-h{w.h}-k{w.k}-s{w.n_shared}x{w.h_shared}"
+                              + ("-lean" if ln else "") + ("-merged" if mg else "") for w, ln, mg in RANDOM_LAYERS])
+def test_layer_random_shapes(xm, wl, lean, merge):
+    """Whole-layer parity on seeded random shapes (the same checks as the
+    named workloads)."""
+    inp = workloads.generate(wl, backward=True)
+    check_layer(xm, wl, inp, f"layer {wl.name}", lean=lean, merge=merge)
+
+
 def check_layer(xm, wl, inp, tag, lean=False, merge=False):
     """The GPU layer against the oracle's layer on the same inputs: routing,
     the PFT, y, dX, the routing weights' gradient, the shared and routed weight

@@ -185,8 +185,15 @@ def test_build_pft_zero_tokens(xm):
 
 # ------------------------------------------------------------------ dispatch / combine
 
+# Rows of fewer 16-byte vectors than slots per token (d / 8 < k in bf16,
+# d / 4 < k in fp32), more than 64 slots, and a last pass over the row that
+# leaves lanes idle while slots beyond them remain: each lane holds one slot's
+# row index, which the others read by shuffle.
+NARROW = [("bf16", 1031, 40, 56, 7), ("f32", 100, 16, 8, 6), ("bf16", 5, 16, 128, 100), ("bf16", 20, 2400, 64, 60)]
+
+
 @pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 16, 6), ("f32", 256, 128, 8, 2),
-                                           ("bf16", 1, 2048, 64, 6), ("bf16", 4096, 7168, 256, 8)])
+                                           ("bf16", 1, 2048, 64, 6), ("bf16", 4096, 7168, 256, 8)] + NARROW)
 def test_dispatch_exact(xm, dtype, T, d, E, k):
     ids, w = workloads.random_topk(T, E, k, seed=3)
     x = workloads.random_rows(T, d, dtype, seed=4)
@@ -200,7 +207,8 @@ def test_dispatch_exact(xm, dtype, T, d, E, k):
 
 
 @pytest.mark.parametrize("dtype,T,d,E,k,with_add", [("bf16", 300, 256, 16, 6, True), ("f32", 256, 128, 8, 2, False),
-                                                    ("bf16", 777, 520, 40, 8, False), ("bf16", 2, 64, 8, 8, True)])
+                                                    ("bf16", 777, 520, 40, 8, False), ("bf16", 2, 64, 8, 8, True)]
+                         + [c + (i % 2 == 0,) for i, c in enumerate(NARROW)])
 def test_combine(xm, dtype, T, d, E, k, with_add):
     ids, w = workloads.random_topk(T, E, k, seed=11)
     pft = _gpu_pft(xm, ids, w, E)
@@ -214,7 +222,8 @@ def test_combine(xm, dtype, T, d, E, k, with_add):
     assert_close(host(y), want, RTOL[dtype] if dtype == "bf16" else 1e-5, "y")
 
 
-@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 16, 6), ("f32", 256, 128, 8, 2), ("bf16", 513, 2048, 64, 6)])
+@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 16, 6), ("f32", 256, 128, 8, 2), ("bf16", 513, 2048, 64, 6)]
+                         + NARROW)
 def test_combine_bwd(xm, dtype, T, d, E, k):
     ids, w = workloads.random_topk(T, E, k, seed=21)
     pft = _gpu_pft(xm, ids, w, E)
@@ -231,7 +240,8 @@ def test_combine_bwd(xm, dtype, T, d, E, k):
 
 
 @pytest.mark.parametrize("dtype,T,d,E,k,with_add", [("bf16", 300, 256, 16, 6, True), ("f32", 256, 128, 8, 2, True),
-                                                    ("bf16", 1000, 1024, 128, 8, False)])
+                                                    ("bf16", 1000, 1024, 128, 8, False)]
+                         + [c + (i % 2 == 1,) for i, c in enumerate(NARROW)])
 def test_dispatch_bwd(xm, dtype, T, d, E, k, with_add):
     ids, w = workloads.random_topk(T, E, k, seed=31)
     pft = _gpu_pft(xm, ids, w, E)
