@@ -161,7 +161,7 @@ def pft_contract(pft: dict, ids: np.ndarray, w: np.ndarray, E: int, orc_mod) -> 
     pft_invariants(ids, w, E, pft)
 
 
-def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2):
+def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2, w13=None):
     """Root-sum-square error scales of one expert's weight gradients.
 
     dW1 = x^T dH1 with dH1 = dA*H3*g(H1), g(a) = sig(a)(1 + a(1 - sig(a))):
@@ -173,10 +173,24 @@ def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2):
     terms dYe*W2 (not |dA|, which may cancel), so the magnitude used for dA is
     |dA| + sqrt(dYe^2 . (W2^2)^T).  dW2 = act^T dYe carries the rounding of act
     and dYe.  The scales are the root-sum-square over rows of those
-    magnitudes; every input is an oracle (fp64) value or a generator input."""
+    magnitudes; every input is an oracle (fp64) value or a generator input.
+
+    fp32 inputs (w13 = (W1, W3) given): H1 and H3 are kept unrounded, so their
+    error is that of summing their d products in fp32, whose scale is the
+    root-sum-square of the products, s = sqrt(x^2 . W^2), not |H| (which may
+    cancel; relative rounding of the stored value is negligible there).  The
+    magnitudes become |H1| + s1 and |H3| + s3; dH1 also carries H1's error
+    through g (|g'| <= 0.5), and act = silu(H1) H3 carries both."""
     w2 = np.asarray(w2, np.float64)
     dam = np.abs(da) + np.sqrt(np.maximum((dye * dye) @ (w2 * w2).T, 0.0))
-    return (rss_rows(x, dam * np.abs(h3)), rss_rows(x, dam * np.abs(h1)), rss_rows(act, dye))
+    a1, a3 = np.abs(h1), np.abs(h3)
+    if w13 is None:
+        return (rss_rows(x, dam * a3), rss_rows(x, dam * a1), rss_rows(act, dye))
+    x2 = np.asarray(x, np.float64) ** 2
+    s1 = np.sqrt(np.maximum(x2 @ (np.asarray(w13[0], np.float64) ** 2), 0.0))
+    s3 = np.sqrt(np.maximum(x2 @ (np.asarray(w13[1], np.float64) ** 2), 0.0))
+    return (rss_rows(x, dam * (a3 + s3 + a3 * s1)), rss_rows(x, dam * (a1 + s1)),
+            rss_rows(np.abs(act) + s1 * a3 + a1 * s3, dye))
 
 
 def assert_wgrad_close(got, ref, rows_of, floors_of, rtol: float, name: str):

@@ -97,7 +97,7 @@ def test_fp32_weight_gradients(xm, dtype, rows, d, h, E, empty):
         if e not in scales:
             sl = slice(o[e], o[e + 1])
             scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl],
-                                            G[sl], host(w2[e]))
+                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
         return scales[e]
 
     rt = RTOL[dtype]

@@ -98,6 +98,25 @@ def test_router_bf16_small(xm, name):
     assert_close(host(w)[ok], r["topk_w"][ok], 1e-4, "topk_w")
 
 
+def _random_routers(n: int, seed: int):
+    """Seeded routing shapes: bf16 with d and E multiples of 8 (the fused
+    kernel up to 64 experts, the split product above), fp32 with any d and E,
+    up to 1024 experts and k up to 64 or k = E."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        dt = "f32" if i % 3 == 2 else "bf16"
+        E = 8 * int(rs.randint(1, 129)) if dt == "bf16" else int(rs.randint(1, 1025))
+        k = E if rs.rand() < 0.1 and E <= 128 else int(rs.randint(1, min(E, 64) + 1))
+        T = int(rs.choice([1, 5, 64, 300, 1031, 4097]))
+        d = 8 * int(rs.randint(1, 513)) if dt == "bf16" else int(rs.randint(1, 600))
+        out.append((dt, T, d, E, k))
+    return out
+
+
+RANDOM_ROUTERS = _random_routers(12, 9)
+
+
 @pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 300, 256, 384, 16), ("bf16", 130, 128, 1024, 8),
                                           ("f32", 257, 64, 10, 3), ("f32", 100, 32, 300, 5),
                                           ("f32", 64, 16, 1021, 4), ("f32", 33, 8, 1, 1),
@@ -106,7 +125,7 @@ def test_router_bf16_small(xm, name):
                                           ("bf16", 4097, 2048, 64, 6), ("bf16", 257, 7168, 128, 8),
                                           ("bf16", 100, 512, 72, 8), ("bf16", 65, 136, 120, 4),
                                           ("bf16", 300, 7168, 48, 6), ("bf16", 50, 8, 16, 4),
-                                          ("bf16", 40, 24, 64, 64)])
+                                          ("bf16", 40, 24, 64, 64)] + RANDOM_ROUTERS)
 def test_router_expert_counts(xm, dtype, T, d, E, k):
     """Expert counts beyond the workloads': more than 256 experts (16 and 32
     lanes per token in the top-k), fp32 counts that are not a multiple of 4
@@ -137,9 +156,24 @@ def test_router_expert_counts(xm, dtype, T, d, E, k):
 
 # ------------------------------------------------------------------ PFT
 
+def _random_pfts(n: int, seed: int):
+    """Seeded buffer shapes: up to 40000 tokens, 1-1024 experts, k up to 32."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for _ in range(n):
+        E = int(rs.randint(1, 1025))
+        out.append((int(rs.choice([1, 2, 63, 500, 4097, 40000])), E, int(rs.randint(1, min(E, 32) + 1)),
+                    float(rs.choice([0.0, 1.0, 2.5]))))
+    return out
+
+
+RANDOM_PFTS = _random_pfts(10, 10)
+
+
 @pytest.mark.parametrize("T,E,k,skew", [(1, 8, 2, 0.0), (255, 8, 2, 0.0), (256, 64, 6, 0.0), (257, 64, 6, 0.0),
                                         (1000, 128, 8, 2.5), (3000, 160, 8, 0.0), (700, 1024, 16, 1.0),
-                                        (64, 8, 8, 0.0), (32768, 160, 8, 0.0), (16384, 128, 8, 3.0)])
+                                        (64, 8, 8, 0.0), (32768, 160, 8, 0.0), (16384, 128, 8, 3.0)]
+                         + RANDOM_PFTS)
 def test_build_pft_bit_exact(xm, T, E, k, skew):
     ids, w = workloads.random_topk(T, E, k, seed=T * 7 + E, skew=skew)
     pft = _gpu_pft(xm, ids, w, E)
@@ -273,6 +307,28 @@ FFN_CASES = [
 ]
 
 
+def _random_ffn_cases(n: int, seed: int):
+    """Seeded expert-FFN shapes: widths that are multiples of 8 down to 8 and
+    rarely of a tile, 1-64 experts with empty and ragged segments, and up to
+    5000 rows (the 256-row tiles from 1024 rows per expert).  A cap on
+    rows*d*h keeps the fp64 oracle to seconds."""
+    rs = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        dt = "f32" if len(out) % 4 == 3 else "bf16"
+        E = int(rs.choice([1, 2, 3, 5, 8, 13, 32, 64]))
+        rows = int(rs.choice([1, 5, 64, 129, 300, 1000, 2500, 5000]))
+        d, h = 8 * int(rs.randint(1, 129)), 8 * int(rs.randint(1, 129))
+        empty = float(rs.choice([0.0, 0.3, 0.7]))
+        if rows * d * h > (5e8 if dt == "bf16" else 1.5e8):
+            continue
+        out.append((dt, rows, d, h, E, empty))
+    return out
+
+
+FFN_CASES += _random_ffn_cases(16, 7)
+
+
 def _ffn_inputs(dtype, rows, d, h, E, empty, seed):
     off = workloads.random_segments(rows, E, seed=seed, empty_frac=empty)
     xs = workloads.random_rows(rows, d, dtype, seed=seed + 1)
@@ -336,6 +392,27 @@ GATHER_CASES = [
     ("bf16", 129, 128, 128, 1, 1, 0.0),
     ("bf16", 400, 192, 512, 8, 4, 0.8),    # h a multiple of 256 below 1024 rows per expert
 ]
+
+
+def _random_gather_cases(n: int, seed: int):
+    """Seeded shapes for the products that read rows through the PFT: as the
+    FFN cases above, with tokens, slots per token and a routing skew."""
+    rs = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        dt = "f32" if len(out) % 4 == 3 else "bf16"
+        E = int(rs.choice([1, 4, 8, 16, 40, 64, 128]))
+        k = int(rs.randint(1, min(E, 8) + 1))
+        T = int(rs.choice([1, 3, 50, 300, 777, 1500]))
+        d, h = 8 * int(rs.randint(1, 129)), 8 * int(rs.randint(1, 129))
+        skew = float(rs.choice([0.0, 0.7, 1.5]))
+        if T * k * d * h > (5e8 if dt == "bf16" else 1.5e8):
+            continue
+        out.append((dt, T, d, h, E, k, skew))
+    return out
+
+
+GATHER_CASES += _random_gather_cases(12, 8)
 
 
 @pytest.mark.parametrize("dtype,T,d,h,E,k,skew", GATHER_CASES)
@@ -438,7 +515,7 @@ def test_expert_ffn_bwd_dw13_gather(xm, dtype, T, d, h, E, k, skew):
         if e not in scales:
             sl = slice(off[e], off[e + 1])
             scales[e] = swiglu_wgrad_scales(Xr[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl],
-                                            G[sl], host(w2[e]))
+                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
         return scales[e]
 
     rows = lambda e: off[e + 1] - off[e]
@@ -574,7 +651,7 @@ def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
         if e not in scales:
             sl = slice(o[e], o[e + 1])
             scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl], G[sl],
-                                            host(w2[e]))
+                                            host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
         return scales[e]
 
     rows = lambda e: o[e + 1] - o[e]
@@ -605,10 +682,27 @@ def test_expert_ffn_zero_rows(xm):
 
 # ------------------------------------------------------------------ router backward
 
+def _random_route_bwd(n: int, seed: int):
+    """Seeded gate-backward shapes: as the routing ones, k up to 128."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        dt = "f32" if i % 3 == 2 else "bf16"
+        E = 8 * int(rs.randint(1, 129)) if dt == "bf16" else int(rs.randint(1, 1025))
+        k = int(rs.randint(1, min(E, 128) + 1))
+        T = int(rs.choice([1, 5, 64, 300, 1031, 4097]))
+        d = 8 * int(rs.randint(1, 257)) if dt == "bf16" else int(rs.randint(1, 400))
+        out.append((dt, T, d, E, k, float(rs.choice([0.5, 1.0, 2.0]))))
+    return out
+
+
+RANDOM_ROUTE_BWD = _random_route_bwd(10, 14)
+
+
 @pytest.mark.parametrize("dtype,T,d,E,k,inv_tau", [("f32", 256, 128, 8, 2, 1.0), ("bf16", 300, 256, 16, 6, 1.0),
                                                    ("bf16", 2500, 512, 160, 8, 2.0), ("bf16", 777, 448, 64, 6, 1.0),
                                                    ("bf16", 600, 256, 256, 8, 1.0), ("f32", 40, 32, 320, 70, 1.0),
-                                                   ("bf16", 64, 64, 512, 100, 0.5)])
+                                                   ("bf16", 64, 64, 512, 100, 0.5)] + RANDOM_ROUTE_BWD)
 def test_route_bwd(xm, dtype, T, d, E, k, inv_tau):
     """Includes 256 experts (the 2x2-wave 256-column tile of Wg's gradient), and
     k above 64 (a token's slots read in two chunks)."""
