@@ -39,6 +39,24 @@ def _pilots(xm, ids, E, P):
     return {key: host(v) for key, v in out.items()}
 
 
+def _divisors(n: int):
+    return [q for q in range(1, n + 1) if n % q == 0]
+
+
+def _random_ep(n: int, seed: int):
+    """Seeded (T, E, k, divisor of E, seed) shapes: up to 1024 experts, k up to
+    32, up to 3000 tokens; T*k at most 40000 keeps the pure-Python plans of
+    the oracle to seconds."""
+    rs = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        E = int(rs.randint(1, 1025))
+        T, k = int(rs.choice([1, 2, 77, 256, 257, 3000])), int(rs.randint(1, min(E, 32) + 1))
+        if T * k <= 40000:
+            out.append((T, E, k, int(rs.choice(_divisors(E))), 100 + len(out)))
+    return out
+
+
 @pytest.mark.parametrize("T,E,k,P,seed", [
     (300, 16, 6, 4, 0),       # small, several blocks of 256 tokens and a ragged tail
     (1, 8, 3, 2, 1),
@@ -46,7 +64,7 @@ def _pilots(xm, ids, E, P):
     (257, 32, 4, 1, 3),       # one expert per node: the pilots are the buffer's rows
     (4096, 64, 6, 8, 4),      # DeepSeek-MoE-16B shape, 8 nodes of 8 experts
     (8192, 256, 8, 32, 5),    # DeepSeek-V3 shape, 8 nodes of 32 experts
-])
+] + _random_ep(10, 20))
 def test_pilots_match_oracle(xm, T, E, k, P, seed):
     ids, _ = workloads.random_topk(T, E, k, seed=seed)
     got = _pilots(xm, ids, E, P)
@@ -67,7 +85,7 @@ def test_pilots_empty(xm):
 
 
 @pytest.mark.parametrize("T,E,k,G,seed", [(300, 16, 6, 4, 0), (64, 8, 8, 8, 1), (4096, 64, 6, 8, 2),
-                                          (10, 12, 3, 3, 3)])
+                                          (10, 12, 3, 3, 3)] + _random_ep(8, 21))
 def test_send_plan_matches_oracle(xm, T, E, k, G, seed):
     ids, w = workloads.random_topk(T, E, k, seed=seed)
     pft = xm.PFT(T, E, k)
@@ -93,12 +111,23 @@ def _recv_plan(xm, C):
     return {key: host(v)[:n] if key in ("local_to_recv", "recv_to_local") else host(v) for key, v in out.items()}
 
 
+def _random_recv(seed: int):
+    """Seeded receive-count matrices: 1-200 ranks, up to 1024 cells, counts up
+    to 100 per cell, some cells empty."""
+    rs = np.random.RandomState(seed)
+    return [(G, int(rs.randint(1, 1024 // G + 1)), int(rs.randint(1, 100)), float(rs.choice([0.0, 0.3, 0.9])), 100 + i)
+            for i, G in enumerate([1, 2, 5, 7, 16, 31, 64, 200])]
+
+
+RANDOM_RECV = _random_recv(30)
+
+
 @pytest.mark.parametrize("G,el,hi,zero_frac,seed", [
     (4, 4, 40, 0.2, 0), (1, 16, 30, 0.1, 1), (8, 1, 50, 0.3, 2), (3, 5, 7, 0.5, 3),
     (8, 8, 900, 0.0, 4),       # DeepSeek-MoE-16B on 8 ranks: ~380 rows per (source, expert)
     (32, 32, 40, 0.1, 5),      # 1024 cells, the most the plan supports
     (2, 3, 1, 1.0, 6),         # nothing received
-])
+] + RANDOM_RECV)
 def test_recv_plan_matches_oracle(xm, G, el, hi, zero_frac, seed):
     rng = np.random.default_rng(seed)
     C = rng.integers(0, hi + 1, size=(G, el)).astype(np.int32)
@@ -110,13 +139,13 @@ def test_recv_plan_matches_oracle(xm, G, el, hi, zero_frac, seed):
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
-def test_scatter_rows_is_the_indexed_copy(xm, dt):
+@pytest.mark.parametrize("n,d,rows", [(1000, 264, 1200), (1, 8, 3), (3000, 8, 3100), (257, 2056, 300)])
+def test_scatter_rows_is_the_indexed_copy(xm, dt, n, d, rows):
     g = torch.Generator().manual_seed(0)
-    n, d, rows = 1000, 264, 1200
     src = torch.randn(n, d, generator=g).to(dt).cuda()
     perm = torch.randperm(rows, generator=g)[:n].to(torch.int32)
-    perm[::97] = -1            # skipped
-    perm[5] = rows + 3         # skipped
+    perm[1::97] = -1           # skipped
+    perm[5::211] = rows + 3    # skipped
     dst = torch.full((rows, d), 7.0, dtype=dt, device="cuda")
     xm.xmoe_scatter_rows(src, perm.cuda(), dst)
     torch.cuda.synchronize()

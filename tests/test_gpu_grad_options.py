@@ -32,6 +32,23 @@ CASES = [
 ]
 
 
+def _random_cases(n: int, seed: int):
+    """Seeded shapes as the expert-FFN parity cases: widths down to 8, 1-64
+    experts with empty and ragged segments."""
+    rs = np.random.RandomState(seed)
+    out = []
+    while len(out) < n:
+        dt = "f32" if len(out) % 3 == 2 else "bf16"
+        rows, E = int(rs.choice([1, 64, 300, 1000, 2500])), int(rs.choice([1, 3, 8, 13, 64]))
+        d, h = 8 * int(rs.randint(1, 97)), 8 * int(rs.randint(1, 97))
+        if rows * d * h <= (3e8 if dt == "bf16" else 1e8):
+            out.append((dt, rows, d, h, E, float(rs.choice([0.0, 0.3, 0.7]))))
+    return out
+
+
+CASES += _random_cases(6, 15)
+
+
 @pytest.fixture(scope="module")
 def xm():
     need_gpu()

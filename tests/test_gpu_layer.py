@@ -250,6 +250,20 @@ def test_side_stream_matches_serial_bitwise(xm, merge):
         assert torch.equal(ga, b.grads()[key]), key
 
 
+@pytest.mark.parametrize("wl", [w for w, _, _ in RANDOM_LAYERS[:12]], ids=[w.name for w, _, _ in RANDOM_LAYERS[:12]])
+def test_layer_variants_bitwise_random(xm, wl):
+    """On seeded random shapes: the overlapped streams give the serial call
+    order's results and the lean layer the saved layer's, bit for bit."""
+    inp = workloads.generate(wl, backward=True)
+    a = run_layer(xm, wl, inp, overlap=False)
+    ya, ga = a.y.clone(), {key: v.clone() for key, v in a.grads().items()}
+    for kw in (dict(overlap=True), dict(lean=True)):
+        b = run_layer(xm, wl, inp, **kw)
+        assert torch.equal(ya, b.y), kw
+        for key, g in ga.items():
+            assert torch.equal(g, b.grads()[key]), (key, kw)
+
+
 def test_layer_is_deterministic(xm):
     """No floating-point atomics: two runs give bitwise identical results."""
     wl = workloads.small("long_batch")
