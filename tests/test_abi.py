@@ -183,3 +183,49 @@ def test_noalloc_pft_build_limit_on_host(xm):
     assert b"scratch" in xm._lib_last_error()
     assert xm._lib_pft_na(p, p, 100, 64, 65, ctypes.byref(pft), None) == 1      # k > E
     assert xm._lib_pft_na(None, p, 100, 64, 6, ctypes.byref(pft), None) == 1
+
+
+def test_binding_checks_tensor_shapes_before_calling(xm):
+    """The binding passes pointers and sizes; it takes the sizes from the
+    inputs and requires every other tensor of the call to hold exactly them,
+    in the call's dtype, so a mismatched output raises instead of being written
+    past.  (CPU tensors of the right shapes pass these checks and are then
+    refused as host memory, also before any call.)"""
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    E, d, h, rows = 4, 64, 32, 10
+    xs = torch.zeros(rows, d, dtype=bf)
+    w1, w3 = torch.zeros(E, d, h, dtype=bf), torch.zeros(E, d, h, dtype=bf)
+    w2 = torch.zeros(E, h, d, dtype=bf)
+    off = torch.zeros(E + 1, dtype=i32)
+    act, ye = torch.zeros(rows, h, dtype=bf), torch.zeros(rows, d, dtype=bf)
+    with pytest.raises(ValueError, match="act"):
+        xm.xmoe_expert_ffn_up(xs, w1, w3, off, torch.zeros(rows - 1, h, dtype=bf))
+    with pytest.raises(ValueError, match="h13"):
+        xm.xmoe_expert_ffn_up(xs, w1, w3, off, act, torch.zeros(rows, h, dtype=bf))
+    with pytest.raises(TypeError, match="act"):
+        xm.xmoe_expert_ffn_up(xs, w1, w3, off, torch.zeros(rows, h, dtype=f32))
+    with pytest.raises(ValueError, match="w3"):
+        xm.xmoe_expert_ffn_up(xs, w1, torch.zeros(E, d, h + 8, dtype=bf), off, act)
+    with pytest.raises(ValueError, match="expert_offsets"):
+        xm.xmoe_expert_ffn(xs, w1, w3, w2, torch.zeros(E, dtype=i32), act, ye)
+    with pytest.raises(ValueError, match="ye"):
+        xm.xmoe_expert_ffn_down(act, w2, off, torch.zeros(rows, d + 8, dtype=bf))
+    with pytest.raises(ValueError, match="dw2"):
+        xm.xmoe_expert_ffn_bwd_dw2(act, ye, off, torch.zeros(E, d, h, dtype=f32))
+    T, k = 5, 2
+    pft = xm.PFT(T, E, k, device="cpu")
+    ids, w = torch.zeros(T, k, dtype=i32), torch.zeros(T, k, dtype=f32)
+    with pytest.raises(ValueError, match="pft.tokens_per_expert"):
+        xm.xmoe_build_pft(ids, w, E + 1, pft, torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="y"):
+        xm.xmoe_combine(torch.zeros(T * k, d, dtype=bf), pft, T, torch.zeros(T + 1, d, dtype=bf))
+    with pytest.raises(ValueError, match="dtopk_w"):
+        xm.xmoe_combine_bwd(torch.zeros(T, d, dtype=bf), torch.zeros(T * k, d, dtype=bf), pft,
+                            torch.zeros(T * k, d, dtype=bf), torch.zeros(T, k + 1, dtype=f32))
+    with pytest.raises(TypeError, match="topk_ids"):
+        xm.xmoe_route(torch.zeros(T, d, dtype=bf), torch.zeros(d, E, dtype=bf), k, w, w,
+                      torch.zeros(T, E, dtype=f32))
+    # the right shapes pass the checks and reach the device-memory check
+    with pytest.raises(ValueError, match="device tensors"):
+        xm.xmoe_expert_ffn(xs, w1, w3, w2, off, act, ye)

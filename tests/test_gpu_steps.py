@@ -566,7 +566,7 @@ def test_expert_ffn_bwd_dact_gather(xm, dtype, T, d, h, E, k, skew):
     assert_close(got[:, h:], ref["dh3"], rt, "dh3")
     # the two-call path: dye = w * dy[token] rounded to the input dtype, then dA
     dye_d = torch.empty((R, d), dtype=tdt, device="cuda")
-    dtw = torch.empty(R, dtype=torch.float32, device="cuda")
+    dtw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     pft = xm.PFT(T, E, k)
     for name, t in pft.fields().items():
         t.copy_(torch.from_numpy(ref_pft[name]))
@@ -736,8 +736,10 @@ def test_rejects_bad_arguments_without_launching(xm):
     with pytest.raises(xm.XmoeError) as e:
         xm.xmoe_route(x, wg, 2, ids, w, lg)
     assert e.value.status == 2
+    ids9 = torch.empty((8, 9), dtype=torch.int32, device="cuda")
+    w9 = torch.empty((8, 9), dtype=torch.float32, device="cuda")
     with pytest.raises(xm.XmoeError) as e:
-        xm.xmoe_route(x[:, :8].contiguous(), wg[:8].contiguous(), 9, ids, w, lg)   # k > E
+        xm.xmoe_route(x[:, :8].contiguous(), wg[:8].contiguous(), 9, ids9, w9, lg)   # k > E
     assert e.value.status == 1
     pft = xm.PFT(8, 8, 2)
     small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
