@@ -26,7 +26,7 @@ def _bits(t: torch.Tensor) -> bytes:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().tobytes()
 
 
-@pytest.mark.parametrize("T,d,E,h,k", [(300, 256, 16, 136, 4), (1000, 512, 128, 128, 8)])
+@pytest.mark.parametrize("T,d,E,h,k", [(300, 256, 16, 136, 4), (1000, 512, 128, 128, 8), (1031, 40, 56, 344, 7)])
 def test_c_driver_matches_python_layer(tmp_path, T, d, E, h, k):
     need_gpu()
     assert os.path.exists(EXE), "tests/c_abi/layer_c is not built (__graft_entry__.build() builds it)"

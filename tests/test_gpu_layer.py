@@ -6,6 +6,8 @@ The GPU chain (route -> PFT -> gathered experts -> combine, and back) runs
 on its own intermediate results; the oracle runs its own slot-order chain on
 the same generator inputs and never sees a GPU value.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -262,6 +264,39 @@ def test_layer_variants_bitwise_random(xm, wl):
         assert torch.equal(ya, b.y), kw
         for key, g in ga.items():
             assert torch.equal(g, b.grads()[key]), (key, kw)
+
+
+@pytest.mark.parametrize("name,lean,merge", [("dsmoe16b", False, False), ("zipf_skew", True, False),
+                                             ("dsmoe16b", False, True)])
+def test_second_step_matches_a_fresh_layer(xm, name, lean, merge):
+    """A layer object reused for a second step with other inputs (other
+    routing, other expert loads) gives bitwise what a fresh layer gives on
+    those inputs: nothing of the first step survives in its buffers."""
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+    wl = workloads.small(name)
+    wl2 = dataclasses.replace(wl, seed=wl.seed + 77)
+    inp1 = workloads.generate(wl, backward=True)
+    inp2 = workloads.generate(wl2, backward=True)
+    g1 = {k: (None if v is None else v.cuda()) for k, v in inp1.items()}
+    g2 = {k: (None if v is None else v.cuda()) for k, v in inp2.items()}
+    weights = {k: g1[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g1}
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean, merge_shared=merge)
+    layer.forward(g1["x"])
+    layer.backward(g1["dy"])
+    ids1 = layer.topk_ids.clone()
+    layer.forward(g2["x"])
+    layer.backward(g2["dy"])
+    torch.cuda.synchronize()
+    fresh = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, lean=lean, merge_shared=merge)
+    fresh.forward(g2["x"])
+    fresh.backward(g2["dy"])
+    torch.cuda.synchronize()
+    assert not torch.equal(ids1, layer.topk_ids)   # the second step routes differently
+    assert torch.equal(layer.y, fresh.y)
+    for key, g in fresh.grads().items():
+        assert torch.equal(layer.grads()[key], g), key
+    for key, t in fresh.pft.fields().items():
+        assert torch.equal(layer.pft.fields()[key], t), key
 
 
 def test_layer_is_deterministic(xm):
