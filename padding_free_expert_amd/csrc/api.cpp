@@ -136,7 +136,7 @@ xmoe::PftPtrs to_ptrs(const xmoe_pft *p) {
 xmoe_status check_gather(const void *x, const int32_t *token_ids, int64_t T, int64_t rows, int32_t d,
                          xmoe_dtype dtype) {
     REQUIRE(rows == 0 || (x && token_ids), XMOE_ERR_INVALID_VALUE, "x and token_ids are required");
-    REQUIRE(T >= 1, XMOE_ERR_INVALID_VALUE, "T must be >= 1");
+    REQUIRE(T >= 0 && (rows == 0 || T >= 1), XMOE_ERR_INVALID_VALUE, "T must be >= 1 when there are rows to gather");
     REQUIRE(T * static_cast<int64_t>(d) * (dtype == XMOE_BF16 ? 2 : 4) < (int64_t{1} << 31), XMOE_ERR_UNSUPPORTED,
             "x must be smaller than 2^31 bytes to be gathered");
     REQUIRE(aligned16(x), XMOE_ERR_UNSUPPORTED, "x must be 16-byte aligned");

@@ -143,11 +143,16 @@ def test_gathered_wgrad_rejects_on_host(xm):
     assert f(None, p, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
     assert f(p, None, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
     assert f(p, p, None, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 1
-    # T < 1, h not a multiple of 8, misaligned x
+    # no tokens but rows to gather, h not a multiple of 8, misaligned x
     assert f(p, p, p, 1, p, 4, 0, 100, 64, 64, p, p, 1, 0, None) == 1
     assert f(p, p, p, 1, p, 4, 100, 100, 64, 12, p, p, 1, 0, None) == 2
     assert f(ctypes.c_void_p(18), p, p, 1, p, 4, 100, 100, 64, 64, p, p, 1, 0, None) == 2
     assert xm._lib_last_error() != b""
+    # an empty batch (no tokens, no rows) passes validation in every gathered
+    # product: what follows is the device check, or nothing to launch
+    assert f(None, None, None, 1, p, 4, 0, 0, 64, 64, p, p, 1, 0, None) not in (1, 2, 3)
+    assert xm._lib_up_g(None, None, p, p, 1, p, 4, 0, 0, 64, 64, None, None, None) not in (1, 2, 3)
+    assert xm._lib_bwd_dact_g(None, None, None, p, None, 1, p, 4, 0, 0, 64, 64, None, None) not in (1, 2, 3)
 
 
 def test_weight_gradient_dtype_and_accumulate_rejected_on_host(xm):

@@ -299,6 +299,31 @@ def test_second_step_matches_a_fresh_layer(xm, name, lean, merge):
         assert torch.equal(layer.pft.fields()[key], t), key
 
 
+@pytest.mark.parametrize("dtype,merge,lean", [("bf16", False, False), ("bf16", True, True), ("f32", False, False)])
+def test_layer_with_no_tokens(xm, dtype, merge, lean):
+    """T = 0: every call is a no-op that still leaves the layer consistent: y
+    and dX are empty, and every weight gradient (routed, shared, gate) is an
+    exact zero, since no token contributes to it."""
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+    wl = workloads.Workload("no_tokens", dtype, T=0, d=64, E=8, h=32, k=2, n_shared=2, h_shared=32, backward=True)
+    inp = workloads.generate(wl, backward=True)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    weights = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2") if k in g}
+    layer = PaddingFreeMoE(weights, 0, wl.k, wl.inv_tau, backward=True, lean=lean, merge_shared=merge)
+    grads = [layer.dW1, layer.dW3, layer.dW2, layer.dwg] + ([] if layer.merged else [layer._ds1, layer._ds3,
+                                                                                       layer._ds2])
+    for t in grads:
+        t.fill_(float("nan"))
+    y = layer.forward(g["x"])
+    dx = layer.backward(g["dy"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, wl.d) and dx.shape == (0, wl.d)
+    for key, t in layer.grads().items():
+        if key in ("dw1", "dw3", "dw2", "ds1", "ds3", "ds2", "dwg"):
+            assert (t == 0).all(), key
+    assert (layer.pft.tokens_per_expert == 0).all() and (layer.pft.expert_offsets == 0).all()
+
+
 def test_layer_is_deterministic(xm):
     """No floating-point atomics: two runs give bitwise identical results."""
     wl = workloads.small("long_batch")
