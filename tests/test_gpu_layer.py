@@ -75,6 +75,11 @@ DEGENERATE = [
     workloads.Workload("one_expert_f32", "f32", T=50, d=64, E=1, h=32, k=1, backward=True),
     workloads.Workload("ragged_widths", "bf16", T=70, d=72, E=16, h=40, k=3, n_shared=1, h_shared=24,
                        backward=True),
+    # the most experts the boundary takes, with many slots per token (split router)
+    workloads.Workload("max_experts", "bf16", T=64, d=64, E=1024, h=32, k=32, backward=True),
+    # every token to all 64 experts through the fused router
+    workloads.Workload("k_equals_E_64", "bf16", T=40, d=64, E=64, h=16, k=64, n_shared=1, h_shared=16,
+                       backward=True),
 ]
 
 
