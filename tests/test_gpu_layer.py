@@ -329,6 +329,40 @@ def test_layer_with_no_tokens(xm, dtype, merge, lean):
     assert (layer.pft.tokens_per_expert == 0).all() and (layer.pft.expert_offsets == 0).all()
 
 
+def _layer_outputs(layer):
+    out = {"y": layer.y.clone()}
+    out.update({key: g.clone() for key, g in layer.grads().items()})
+    return out
+
+
+@pytest.mark.parametrize("name,merge,lean", [("dsmoe16b", False, False), ("dsmoe16b", True, False),
+                                             ("zipf_skew", False, True)])
+def test_layer_on_a_caller_stream(xm, name, merge, lean):
+    """The layer on a stream the caller passes (its side streams forked from
+    and joined into that stream) gives bitwise the results on the current
+    stream."""
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+    wl = workloads.small(name)
+    inp = workloads.generate(wl, backward=True)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    weights = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g}
+    layer = PaddingFreeMoE(weights, wl.T, wl.k, wl.inv_tau, backward=True, merge_shared=merge, lean=lean)
+    layer.forward(g["x"])
+    layer.backward(g["dy"])
+    torch.cuda.synchronize()
+    ref = _layer_outputs(layer)
+    for t in [layer.y] + list(layer.grads().values()):
+        t.fill_(float("nan"))
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    layer.forward(g["x"], stream=cs)
+    layer.backward(g["dy"], stream=cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    for key, v in _layer_outputs(layer).items():
+        assert torch.equal(v, ref[key]), key
+
+
 def test_layer_is_deterministic(xm):
     """No floating-point atomics: two runs give bitwise identical results."""
     wl = workloads.small("long_batch")
