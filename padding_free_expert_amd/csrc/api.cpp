@@ -73,6 +73,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
+// a * b <= limit for a, b >= 0, without forming a product that could overflow
+// (callers may pass any int64 size; the checks must stay defined for all)
+bool within(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b == 0 || a <= limit / b); }
+
 xmoe_status check_dtype(xmoe_dtype dt) {
     if (dt != XMOE_F32 && dt != XMOE_BF16) return fail(XMOE_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
     return XMOE_OK;
@@ -91,7 +95,7 @@ xmoe_status check_pft(const xmoe_pft *pft, bool need_s2r, bool need_w, bool need
 xmoe_status check_rows_common(int64_t T, int32_t d, int32_t k) {
     REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
     REQUIRE(k >= 1 && k <= 1024, XMOE_ERR_INVALID_VALUE, "k must be in [1, 1024]");
-    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    REQUIRE(within(T, k, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
     REQUIRE(d >= 1, XMOE_ERR_INVALID_VALUE, "d must be >= 1");
     REQUIRE(d % 8 == 0, XMOE_ERR_UNSUPPORTED, "d must be a multiple of 8");
     return XMOE_OK;
@@ -137,7 +141,8 @@ xmoe_status check_gather(const void *x, const int32_t *token_ids, int64_t T, int
                          xmoe_dtype dtype) {
     REQUIRE(rows == 0 || (x && token_ids), XMOE_ERR_INVALID_VALUE, "x and token_ids are required");
     REQUIRE(T >= 0 && (rows == 0 || T >= 1), XMOE_ERR_INVALID_VALUE, "T must be >= 1 when there are rows to gather");
-    REQUIRE(T * static_cast<int64_t>(d) * (dtype == XMOE_BF16 ? 2 : 4) < (int64_t{1} << 31), XMOE_ERR_UNSUPPORTED,
+    REQUIRE(within(T, static_cast<int64_t>(d) * (dtype == XMOE_BF16 ? 2 : 4), (int64_t{1} << 31) - 1),
+            XMOE_ERR_UNSUPPORTED,
             "x must be smaller than 2^31 bytes to be gathered");
     REQUIRE(aligned16(x), XMOE_ERR_UNSUPPORTED, "x must be 16-byte aligned");
     return XMOE_OK;
@@ -160,7 +165,7 @@ xmoe_status xmoe_query_device(int ordinal, int *is_gfx950) {
 }
 
 size_t xmoe_route_workspace_size(int64_t T, int32_t d, int32_t E, xmoe_dtype dtype) {
-    if (T < 0 || d < 1 || E < 1 || E > 1024 || (dtype != XMOE_BF16 && dtype != XMOE_F32)) return 0;
+    if (T < 0 || T > kMaxRows || d < 1 || E < 1 || E > 1024 || (dtype != XMOE_BF16 && dtype != XMOE_F32)) return 0;
     return xmoe::route_workspace(T, d, E, dtype);
 }
 
@@ -173,7 +178,7 @@ xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t 
     REQUIRE(T >= 0 && d >= 1, XMOE_ERR_INVALID_VALUE, "T must be >= 0 and d >= 1");
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
-    REQUIRE(T * static_cast<int64_t>(E) <= kMaxRows * 8 && T <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T too large");
+    REQUIRE(T <= kMaxRows && within(T, E, kMaxRows * 8), XMOE_ERR_INVALID_VALUE, "T too large");
     if (dtype == XMOE_BF16) {
         REQUIRE(d % 8 == 0 && E % 8 == 0, XMOE_ERR_UNSUPPORTED, "bf16 routing needs d and E multiples of 8");
         REQUIRE(aligned16(x) && aligned16(wg), XMOE_ERR_UNSUPPORTED, "x and wg must be 16-byte aligned");
@@ -189,7 +194,7 @@ xmoe_status xmoe_route(const void *x, const void *wg, xmoe_dtype dtype, int64_t 
 }
 
 size_t xmoe_build_pft_workspace_size(int64_t T, int32_t E, int32_t k) {
-    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || T * static_cast<int64_t>(k) > kMaxRows) return 0;
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || !within(T, k, kMaxRows)) return 0;
     return xmoe::pft_workspace(T, E);
 }
 
@@ -199,7 +204,7 @@ xmoe_status xmoe_build_pft(const int32_t *topk_ids, const float *topk_w, int64_t
     REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
-    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    REQUIRE(within(T, k, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
     TRY(check_pft(pft, T > 0, T > 0, T > 0));
     REQUIRE(pft->tokens_per_expert && pft->expert_offsets, XMOE_ERR_INVALID_VALUE,
             "pft->tokens_per_expert and pft->expert_offsets are required");
@@ -219,7 +224,7 @@ xmoe_status xmoe_build_pft_noalloc(const int32_t *topk_ids, const float *topk_w,
     REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
-    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    REQUIRE(within(T, k, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
     TRY(check_pft(pft, T > 0, T > 0, T > 0));
     REQUIRE(pft->tokens_per_expert && pft->expert_offsets, XMOE_ERR_INVALID_VALUE,
             "pft->tokens_per_expert and pft->expert_offsets are required");
@@ -241,7 +246,7 @@ xmoe_status xmoe_build_pft_shared(const int32_t *topk_ids, const float *topk_w, 
     REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
     REQUIRE(E_routed >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E_routed >= 1 and E_routed + n_shared <= 1024");
     REQUIRE(k >= 1 && k <= E_routed, XMOE_ERR_INVALID_VALUE, "k must be in [1, E_routed]");
-    REQUIRE(T * ks <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*(k+n_shared) must be < 2^31");
+    REQUIRE(within(T, ks, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*(k+n_shared) must be < 2^31");
     TRY(check_pft(pft, T > 0, T > 0, T > 0));
     REQUIRE(pft->tokens_per_expert && pft->expert_offsets, XMOE_ERR_INVALID_VALUE,
             "pft->tokens_per_expert and pft->expert_offsets are required");
@@ -512,7 +517,7 @@ xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits, c
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
     REQUIRE(ldw >= k, XMOE_ERR_INVALID_VALUE, "ldw must be >= k");
-    REQUIRE(T * static_cast<int64_t>(ldw) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*ldw must be < 2^31");
+    REQUIRE(within(T, ldw, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*ldw must be < 2^31");
     if (dtype == XMOE_BF16) {
         REQUIRE(d % 8 == 0 && E % 8 == 0, XMOE_ERR_UNSUPPORTED, "bf16 needs d and E multiples of 8");
         REQUIRE(aligned16(x) && aligned16(wg) && aligned16(dx), XMOE_ERR_UNSUPPORTED,
@@ -530,7 +535,7 @@ xmoe_status xmoe_route_bwd(const void *x, const void *wg, const float *logits, c
 /* ---------------------------------------------- pilot tokens and EP plans */
 
 size_t xmoe_build_pilots_workspace_size(int64_t T, int32_t E, int32_t k, int32_t experts_per_node) {
-    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || T * static_cast<int64_t>(k) > kMaxRows ||
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || !within(T, k, kMaxRows) ||
         experts_per_node < 1 || E % experts_per_node != 0)
         return 0;
     return xmoe::pft_workspace(T, E / experts_per_node);
@@ -543,7 +548,7 @@ xmoe_status xmoe_build_pilots(const int32_t *topk_ids, int64_t T, int32_t E, int
     REQUIRE(T >= 0, XMOE_ERR_INVALID_VALUE, "T must be >= 0");
     REQUIRE(E >= 1 && E <= 1024, XMOE_ERR_INVALID_VALUE, "E must be in [1, 1024]");
     REQUIRE(k >= 1 && k <= E, XMOE_ERR_INVALID_VALUE, "k must be in [1, E]");
-    REQUIRE(T * static_cast<int64_t>(k) <= kMaxRows, XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
+    REQUIRE(within(T, k, kMaxRows), XMOE_ERR_INVALID_VALUE, "T*k must be < 2^31");
     REQUIRE(experts_per_node >= 1 && E % experts_per_node == 0, XMOE_ERR_INVALID_VALUE,
             "experts_per_node must divide E");
     REQUIRE(node_counts && node_offsets, XMOE_ERR_INVALID_VALUE, "node_counts and node_offsets are required");
