@@ -5,7 +5,6 @@ second with a smaller input, so the scratch holds the first call's counts when
 the second starts.  Also its size limit, checked on the host."""
 import ctypes
 
-import numpy as np
 import pytest
 import torch
 
