@@ -374,6 +374,28 @@ def test_layer_is_deterministic(xm):
     assert torch.equal(dw1a, b.dw1)
 
 
+def test_full_size_steps_repeat_bitwise(xm):
+    """Many full-size steps of one layer (the DeepSeek-MoE-16B shape, all its
+    streams overlapped) reproduce the first step's outputs and gradients bit
+    for bit: no race between the streams or inside the kernels shows."""
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+    wl = workloads.get("dsmoe16b")
+    inp = workloads.generate(wl, device="cuda", backward=True)
+    w = {k: inp[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2") if k in inp}
+    layer = PaddingFreeMoE(w, wl.T, wl.k, wl.inv_tau, backward=True)
+    layer.forward(inp["x"])
+    layer.backward(inp["dy"])
+    torch.cuda.synchronize()
+    ref = _layer_outputs(layer)
+    for i in range(60):
+        layer.forward(inp["x"])
+        layer.backward(inp["dy"])
+        if i % 10 == 9:
+            torch.cuda.synchronize()
+            for key, v in _layer_outputs(layer).items():
+                assert torch.equal(v, ref[key]), (i, key)
+
+
 def test_identity_like_combine_k_equals_E(xm):
     """k = E: every token goes to every expert; the PFT is [T]*E rows and the
     layer still matches the oracle."""
