@@ -234,3 +234,23 @@ def test_binding_checks_tensor_shapes_before_calling(xm):
     # the right shapes pass the checks and reach the device-memory check
     with pytest.raises(ValueError, match="device tensors"):
         xm.xmoe_expert_ffn(xs, w1, w3, w2, off, act, ye)
+
+
+def test_every_binding_call_checks_its_tensors():
+    """Every binding function that calls into the library (through _check)
+    first checks the tensors it passes (_shape, _atleast, _ffn_shapes,
+    _pft_sized or an explicit shape test), so no future entry point can pass
+    an unchecked buffer size."""
+    import ast
+    src = open(os.path.join(ROOT, "padding_free_expert_amd", "__init__.py")).read()
+    tree = ast.parse(src)
+    checks = {"_shape", "_atleast", "_ffn_shapes", "_pft_sized"}
+    missing = []
+    for fn in tree.body:
+        if not isinstance(fn, ast.FunctionDef) or not fn.name.startswith("xmoe_"):
+            continue
+        called = {n.func.id for n in ast.walk(fn) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
+        takes_tensors = any(a.arg not in ("stream",) for a in fn.args.args) and "_ptr" in called
+        if "_check" in called and takes_tensors and not (called & checks):
+            missing.append(fn.name)
+    assert not missing, f"binding calls without tensor checks: {missing}"
