@@ -161,7 +161,17 @@ def pft_contract(pft: dict, ids: np.ndarray, w: np.ndarray, E: int, orc_mod) -> 
     pft_invariants(ids, w, E, pft)
 
 
-def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2, w13=None):
+def wgrad_acc(dtype: str, K: int) -> float:
+    """Weight of H1/H3's summation error in the weight-gradient floors, in
+    units of the stored values' rounding (see swiglu_wgrad_scales): fp32 keeps
+    H unrounded, so its error is the fp32 sum's, 1 in units of 2^-24 per
+    root-sum-square of the products; bf16 rounds H to 2^-9 relative, and the
+    fp32 sum over K products adds about 2^-24 sqrt(K) of their rss, which is
+    2^-15 sqrt(K) in bf16 units (taken 4x: 2^-13 sqrt(K))."""
+    return 1.0 if dtype == "f32" else 2.0 ** -13 * float(np.sqrt(K))
+
+
+def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2, w13=None, acc=1.0):
     """Root-sum-square error scales of one expert's weight gradients.
 
     dW1 = x^T dH1 with dH1 = dA*H3*g(H1), g(a) = sig(a)(1 + a(1 - sig(a))):
@@ -175,20 +185,20 @@ def swiglu_wgrad_scales(x, da, h1, h3, act, dye, w2, w13=None):
     and dYe.  The scales are the root-sum-square over rows of those
     magnitudes; every input is an oracle (fp64) value or a generator input.
 
-    fp32 inputs (w13 = (W1, W3) given): H1 and H3 are kept unrounded, so their
-    error is that of summing their d products in fp32, whose scale is the
-    root-sum-square of the products, s = sqrt(x^2 . W^2), not |H| (which may
-    cancel; relative rounding of the stored value is negligible there).  The
-    magnitudes become |H1| + s1 and |H3| + s3; dH1 also carries H1's error
-    through g (|g'| <= 0.5), and act = silu(H1) H3 carries both."""
+    H1 and H3 are sums of d products, whose summation error scales with the
+    root-sum-square of the products, s = sqrt(x^2 . W^2), not with |H|: where
+    H cancels to near zero that error dominates.  With w13 = (W1, W3) given,
+    the magnitudes become |H1| + acc*s1 and |H3| + acc*s3 (acc from
+    wgrad_acc), dH1 also carries H1's error through g (|g'| <= 0.5), and act =
+    silu(H1) H3 carries both."""
     w2 = np.asarray(w2, np.float64)
     dam = np.abs(da) + np.sqrt(np.maximum((dye * dye) @ (w2 * w2).T, 0.0))
     a1, a3 = np.abs(h1), np.abs(h3)
     if w13 is None:
         return (rss_rows(x, dam * a3), rss_rows(x, dam * a1), rss_rows(act, dye))
     x2 = np.asarray(x, np.float64) ** 2
-    s1 = np.sqrt(np.maximum(x2 @ (np.asarray(w13[0], np.float64) ** 2), 0.0))
-    s3 = np.sqrt(np.maximum(x2 @ (np.asarray(w13[1], np.float64) ** 2), 0.0))
+    s1 = acc * np.sqrt(np.maximum(x2 @ (np.asarray(w13[0], np.float64) ** 2), 0.0))
+    s3 = acc * np.sqrt(np.maximum(x2 @ (np.asarray(w13[1], np.float64) ** 2), 0.0))
     return (rss_rows(x, dam * (a3 + s3 + a3 * s1)), rss_rows(x, dam * (a1 + s1)),
             rss_rows(np.abs(act) + s1 * a3 + a1 * s3, dye))
 

@@ -21,7 +21,7 @@ import torch
 import oracle as orc
 import workloads
 from _helpers import (buffer_routing, RTOL, assert_close, by_expert, dx_floor, host, near_tie_bound, need_gpu, orc_in,
-                      pft_contract, report, routing_check, swiglu_wgrad_scales, used_str)
+                      pft_contract, report, routing_check, swiglu_wgrad_scales, used_str, wgrad_acc)
 
 pytestmark = pytest.mark.gpu
 
@@ -184,7 +184,9 @@ def _check_expert_whole(layer, inp, r, e, rt):
     f = orc.ffn(x, z, w1, w3, w2, row_token=tok, want_hidden=True)
     b = orc.ffn_bwd(x, z, w1, w3, w2, dye, row_token=tok, want_dh=True)
     X = host(inp["x"][torch.as_tensor(tok, device="cuda", dtype=torch.long)])
-    f1, f3, f2 = swiglu_wgrad_scales(X, b["da"], f["h1"], f["h3"], f["act"], dye, host(inp["w2"][e]))
+    f1, f3, f2 = swiglu_wgrad_scales(X, b["da"], f["h1"], f["h3"], f["act"], dye, host(inp["w2"][e]),
+                                     (host(inp["w1"][e]), host(inp["w3"][e])),
+                                     wgrad_acc("f32" if layer.dtype == torch.float32 else "bf16", layer.d))
     print(f"  expert {e}: {tok.size} rows, whole gradient", flush=True)
     return {"dw1 small": assert_close(host(layer.dw1[e]), b["dw1"][0], rt, f"dw1[{e}]", floor=f1),
             "dw3 small": assert_close(host(layer.dw3[e]), b["dw3"][0], rt, f"dw3[{e}]", floor=f3),

@@ -17,7 +17,7 @@ import torch
 
 import oracle as orc
 import workloads
-from _helpers import RTOL, assert_close, assert_wgrad_close, host, need_gpu, orc_in, swiglu_wgrad_scales
+from _helpers import RTOL, assert_close, assert_wgrad_close, host, need_gpu, orc_in, swiglu_wgrad_scales, wgrad_acc
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_fp32_weight_gradients(xm, dtype, rows, d, h, E, empty):
         if e not in scales:
             sl = slice(o[e], o[e + 1])
             scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl],
-                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
+                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])), wgrad_acc(dtype, d))
         return scales[e]
 
     rt = RTOL[dtype]

@@ -16,7 +16,7 @@ import oracle as orc
 import workloads
 from _helpers import (buffer_routing, RTOL, assert_close, assert_wgrad_close, by_expert, dx_floor, host, near_tie_bound,
                       need_gpu, orc_in, pft_contract, report, router_wgrad_floor, routing_check, swiglu_wgrad_scales,
-                      used_str)
+                      used_str, wgrad_acc)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,7 +144,6 @@ def check_layer(xm, wl, inp, tag, lean=False, merge=False):
     fwd = orc.layer_forward(o, wl.k, mode, wl.inv_tau, n_shared=wl.n_shared)
     bwd = orc.layer_backward(o, fwd, o["dy"], wl.inv_tau, n_shared=wl.n_shared)
     rt = RTOL[wl.dtype]
-    f32 = wl.dtype == "f32"
     sb = None if inp["select_bias"] is None else inp["select_bias"].numpy()
 
     # routing: exact where unambiguous, valid where near-tied (none expected in fp32)
@@ -194,8 +193,8 @@ def check_layer(xm, wl, inp, tag, lean=False, merge=False):
             f, b = fwd["shared"][s_], bwd["shared"][s_]
             cs = slice(s_ * hs, (s_ + 1) * hs)
             f1, f3, f2 = swiglu_wgrad_scales(X, b["da"], f["h1"], f["h3"], f["act"], host(inp["dy"]),
-                                             host(inp["s2"])[cs, :],
-                                             (host(inp["s1"])[:, cs], host(inp["s3"])[:, cs]) if f32 else None)
+                                             host(inp["s2"])[cs, :], (host(inp["s1"])[:, cs], host(inp["s3"])[:, cs]),
+                                             wgrad_acc(wl.dtype, wl.d))
             cs = slice(s_ * hs, (s_ + 1) * hs)
             u[f"ds1[{s_}]"] = assert_close(host(layer.ds1[0])[:, cs], bwd["ds1"][:, cs], rt, f"ds1[{s_}]", floor=f1)
             u[f"ds3[{s_}]"] = assert_close(host(layer.ds3[0])[:, cs], bwd["ds3"][:, cs], rt, f"ds3[{s_}]", floor=f3)
@@ -209,8 +208,8 @@ def check_layer(xm, wl, inp, tag, lean=False, merge=False):
         if e not in scales:
             r = fwd["row_expert"] == e
             scales[e] = swiglu_wgrad_scales(Xr[r], bwd["da"][r], fwd["h1"][r], fwd["h3"][r], fwd["act"][r],
-                                            bwd["dye"][r], host(inp["w2"][e]),
-                                            (host(inp["w1"][e]), host(inp["w3"][e])) if f32 else None)
+                                            bwd["dye"][r], host(inp["w2"][e]), (host(inp["w1"][e]), host(inp["w3"][e])),
+                                            wgrad_acc(wl.dtype, wl.d))
         return scales[e]
 
     def rows(e):

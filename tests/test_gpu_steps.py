@@ -12,7 +12,7 @@ import torch
 import oracle as orc
 import workloads
 from _helpers import (RTOL, assert_close, assert_wgrad_close, host, need_gpu, orc_in, routing_check, rss_rows,
-                      swiglu_wgrad_scales)
+                      swiglu_wgrad_scales, wgrad_acc)
 
 pytestmark = pytest.mark.gpu
 
@@ -515,7 +515,7 @@ def test_expert_ffn_bwd_dw13_gather(xm, dtype, T, d, h, E, k, skew):
         if e not in scales:
             sl = slice(off[e], off[e + 1])
             scales[e] = swiglu_wgrad_scales(Xr[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl],
-                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
+                                            G[sl], host(w2[e]), (host(w1[e]), host(w3[e])), wgrad_acc(dtype, d))
         return scales[e]
 
     rows = lambda e: off[e + 1] - off[e]
@@ -651,7 +651,7 @@ def test_expert_ffn_backward(xm, dtype, rows, d, h, E, empty):
         if e not in scales:
             sl = slice(o[e], o[e + 1])
             scales[e] = swiglu_wgrad_scales(X[sl], ref["da"][sl], fwd["h1"][sl], fwd["h3"][sl], fwd["act"][sl], G[sl],
-                                            host(w2[e]), (host(w1[e]), host(w3[e])) if dtype == "f32" else None)
+                                            host(w2[e]), (host(w1[e]), host(w3[e])), wgrad_acc(dtype, d))
         return scales[e]
 
     rows = lambda e: o[e + 1] - o[e]
