@@ -395,6 +395,52 @@ def test_full_size_steps_repeat_bitwise(xm):
                 assert torch.equal(v, ref[key]), (i, key)
 
 
+def test_two_layers_at_once_from_two_threads(xm):
+    """Two independent layers, each driven by its own host thread on its own
+    stream at the same time, give bitwise the results each gives alone: the
+    library keeps no state between calls that two users could share."""
+    import threading
+    from padding_free_expert_amd.layer import PaddingFreeMoE
+    made = []
+    for name, seed in (("dsmoe16b", 3), ("zipf_skew", 4)):
+        wl = dataclasses.replace(workloads.small(name), seed=seed)
+        inp = workloads.generate(wl, backward=True)
+        g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+        w = {k: g[k] for k in ("wg", "w1", "w3", "w2", "s1", "s3", "s2", "logit_bias", "select_bias") if k in g}
+        made.append((PaddingFreeMoE(w, wl.T, wl.k, wl.inv_tau, backward=True), g))
+    refs = []
+    for layer, g in made:
+        layer.forward(g["x"])
+        layer.backward(g["dy"])
+        torch.cuda.synchronize()
+        refs.append(_layer_outputs(layer))
+        for t in [layer.y] + list(layer.grads().values()):
+            t.fill_(float("nan"))
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(layer, g):
+        try:
+            st = torch.cuda.Stream()
+            for _ in range(5):
+                layer.forward(g["x"], stream=st)
+                layer.backward(g["dy"], stream=st)
+            st.synchronize()
+        except Exception as e:  # reported below, in the test's thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=lg) for lg in made]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (layer, _), ref in zip(made, refs):
+        for key, v in _layer_outputs(layer).items():
+            assert torch.equal(v, ref[key]), key
+
+
 def test_identity_like_combine_k_equals_E(xm):
     """k = E: every token goes to every expert; the PFT is [T]*E rows and the
     layer still matches the oracle."""
