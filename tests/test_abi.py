@@ -254,3 +254,24 @@ def test_every_binding_call_checks_its_tensors():
         if "_check" in called and takes_tensors and not (called & checks):
             missing.append(fn.name)
     assert not missing, f"binding calls without tensor checks: {missing}"
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """A copy of the package without libxmoe.so refuses to import (no CPU or
+    PyTorch fallback), and no product source imports or loads the oracle."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "padding_free_expert_amd")
+    dst = tmp_path / "padding_free_expert_amd"
+    dst.mkdir()
+    for f in ("__init__.py", "layer.py"):
+        shutil.copy(os.path.join(pkg, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import padding_free_expert_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr, r.stderr[-2000:]
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp")):
+                src = open(os.path.join(dirpath, f), errors="replace").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|liboracle", src, re.M), f
