@@ -80,6 +80,8 @@ DEGENERATE = [
     # every token to all 64 experts through the fused router
     workloads.Workload("k_equals_E_64", "bf16", T=40, d=64, E=64, h=16, k=64, n_shared=1, h_shared=16,
                        backward=True),
+    # more than 64 slots per token (the row kernels and the gate read them in two chunks), rows of 16
+    workloads.Workload("k_100", "bf16", T=20, d=16, E=128, h=16, k=100, n_shared=1, h_shared=16, backward=True),
 ]
 
 
