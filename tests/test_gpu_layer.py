@@ -82,6 +82,8 @@ DEGENERATE = [
                        backward=True),
     # more than 64 slots per token (the row kernels and the gate read them in two chunks), rows of 16
     workloads.Workload("k_100", "bf16", T=20, d=16, E=128, h=16, k=100, n_shared=1, h_shared=16, backward=True),
+    # a very peaked router: most selected experts' weights underflow towards zero
+    workloads.Workload("peaked", "bf16", T=64, d=64, E=16, h=32, k=4, inv_tau=50.0, backward=True),
 ]
 
 
